@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's sharded mixed-precision optimizer step on one GPU.
+
+A step is one pass of the whole hot path over one batch of resident
+synthetic gradients: shard reduce of the P bf16 replicas with the average,
+overflow count and exact norm (bucketed where the workload says so), the
+gated fused AdamW on fp32 master/m/v with the bf16 param write, and, for the
+30B workload, the MXFP8 pack of the param shard (the all-gather payload).
+
+Prints ONE JSON line: params/s of the shard (whole job = one GPU), HBM GB/s
+against the fused-minimum bytes, the roofline of the dominant kernel measured
+with HIP events inside the timed region, and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C5", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26,
+                    help="elements of the CPU-oracle sample")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    return ap.parse_args()
+
+
+def per_elem_bytes(w, st):
+    """Fused-minimum HBM bytes per shard element, per launch kind."""
+    g_b = w.g_bytes
+    P = w.P
+    if st.path == "fused":
+        kinds = {"adamw": P * g_b + 26}
+    elif st.path == "materialize":
+        kinds = {"reduce": P * g_b + 4, "adamw": 4 + 26}
+    else:
+        kinds = {"reduce": P * g_b, "adamw": P * g_b + 26}
+    if w.pack:
+        kinds["mxfp8_pack"] = 2 + 1 + 1.0 / 32
+    return kinds
+
+
+def cpu_baseline(w, sample, steps):
+    """The CPU oracle, untuned and single-threaded, on the first `sample`
+    elements of the workload's shard (inputs generated beforehand)."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+    sample = min(sample, w.S)
+    start = w.shard_start()
+    master = synth.fill(w.master_spec(), start, sample, False, threads=8)
+    m = np.zeros(sample, np.float32)
+    v = np.zeros(sample, np.float32)
+    param = np.zeros(sample, np.uint16)
+    g_tmp = np.empty(sample, np.float32)
+    reps = [synth.fill(w.grad_spec(1, k), start, sample, w.grad_bf16, threads=8)
+            for k in range(w.P)]
+    inv = O.inv_scale(w.P, w.loss_scale)
+    elem = np.empty(sample, np.uint8) if w.pack else None
+    t0 = time.perf_counter()
+    for t in range(1, steps + 1):
+        O.step(reps, inv, w.max_norm, w.check_overflow, w.lr, w.beta1, w.beta2, w.eps,
+               w.wd, t, master, m, v, param, g_tmp=g_tmp)
+        if w.pack:
+            elem, _ = O.mxfp8_pack(param[: sample // 32 * 32])
+    dt = time.perf_counter() - t0
+    rate = sample * steps / dt
+    return {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sample} elements of the {w.name} shard, {steps} steps, "
+                      f"inputs pre-generated, single thread",
+            "seconds": round(dt, 3), "cpu": platform.processor() or platform.machine(),
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs each rank's shard step "
+              f"on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import zero_sharded_mixed_step_amd as zs
+    from synth import configs
+
+    w = configs.ALL[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = zs.ShardStep(w.S, w.P, torch.bfloat16 if w.grad_bf16 else torch.float32, lr=w.lr,
+                      beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
+                      max_norm=w.max_norm, check_overflow=w.check_overflow,
+                      loss_scale=w.loss_scale, bucket=w.bucket, pack=w.pack, device=dev)
+    start = w.shard_start()
+    synth.fill_device(w.master_spec(), start, st.master)
+    synth.fill_device(w.master_spec(), start, st.param)
+    gdt = torch.int16 if w.grad_bf16 else torch.float32
+    reps = []
+    for k in range(w.P):
+        r = torch.empty(w.S, dtype=gdt, device=dev)
+        synth.fill_device(w.grad_spec(1, k), start, r)
+        reps.append(r)
+    torch.cuda.synchronize()
+
+    kinds = per_elem_bytes(w, st)
+    events = {k: [] for k in kinds}
+
+    def timed(kind, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        events[kind].append((a, b))
+
+    def one_step(record):
+        if not record:
+            st.step(reps)
+            return
+        if st.path == "fused":
+            zs.zero_norm_acc_clear(st.acc)
+        else:
+            timed("reduce", lambda: st.reduce(reps))
+        timed("adamw", lambda: st.update(reps))
+        if w.pack:
+            timed("mxfp8_pack", st.pack_param)
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    applied = st.applied_steps()
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    step_bytes = sum(kinds.values()) * w.S
+    params_per_s = w.S / (elapsed / args.steps)
+    gbps = step_bytes / (elapsed / args.steps) / 1e9
+    kernel_ms = {k: sum(a.elapsed_time(b) for a, b in ev) / len(ev) for k, ev in events.items()}
+    per_kernel = {k: {"avg_ms": round(kernel_ms[k], 4),
+                      "bytes_per_elem": kinds[k],
+                      "gbps": round(kinds[k] * w.S / (kernel_ms[k] * 1e-3) / 1e9, 1)}
+                  for k in kinds}
+    dom = max(kernel_ms, key=kernel_ms.get)
+    dom_gbps = per_kernel[dom]["gbps"]
+    out = {
+        "metric": "optimizer-step params/sec per shard + achieved HBM GB/s (% of peak)",
+        "value": round(params_per_s, 1),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.title}", "shard_elems": w.S, "P": w.P,
+                   "grad_dtype": "bf16" if w.grad_bf16 else "f32", "bucket": w.bucket,
+                   "max_norm": w.max_norm, "check_overflow": w.check_overflow,
+                   "mxfp8_pack": w.pack, "path": st.path},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_param": sum(kinds.values()),
+        "applied_steps": applied,
+        "kernels": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

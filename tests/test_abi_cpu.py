@@ -1,0 +1,82 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments before touching the device.
+No call here launches a kernel."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_step.h")
+LIB = os.path.join(ROOT, "zero_sharded_mixed_step_amd", "libzero_step.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libzero_step.so is not built (run __graft_entry__.build())")
+    return C.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"zero_shard_reduce", "zero_grad_norm", "zero_adamw_step",
+            "zero_mxfp8_pack"} <= set(names)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    lib.zero_abi_version.restype = C.c_int
+    assert lib.zero_abi_version() == 1
+    lib.zero_strerror.restype = C.c_char_p
+    lib.zero_strerror.argtypes = [C.c_int]
+    texts = {lib.zero_strerror(s).decode() for s in (0, -1, -2, -3, -4, 7)}
+    assert len(texts) == 6 and all(texts)
+
+
+def test_inv_scale_matches_definition(lib):
+    lib.zero_inv_scale.restype = C.c_float
+    lib.zero_inv_scale.argtypes = [C.c_int, C.c_double]
+    for P in (1, 2, 3, 4, 7, 8, 64):
+        for ls in (1.0, 65536.0, 1024.0, 3.0):
+            assert lib.zero_inv_scale(P, ls) == O.inv_scale(P, ls)
+
+
+def test_argument_checks(lib):
+    vp = C.c_void_p
+    lib.zero_shard_reduce.argtypes = [vp, C.c_int, C.c_int, C.c_size_t, C.c_float, vp, vp, vp]
+    lib.zero_mxfp8_pack.argtypes = [vp, C.c_size_t, vp, vp, vp]
+    lib.zero_grad_norm.argtypes = [vp, C.c_int, C.c_size_t, C.c_float, vp, vp]
+    lib.zero_adamw_step.argtypes = [vp, vp]
+    lib.zero_norm_acc_clear.argtypes = [vp, C.c_int, vp]
+    fake = 0x10000                     # aligned, never dereferenced
+    reps = (vp * 2)(fake, fake + 0x1000)
+    assert lib.zero_shard_reduce(None, 2, 1, 64, 1.0, fake, None, None) == -1
+    assert lib.zero_shard_reduce(reps, 0, 1, 64, 1.0, fake, None, None) == -1
+    assert lib.zero_shard_reduce(reps, 65, 1, 64, 1.0, fake, None, None) == -1
+    assert lib.zero_shard_reduce(reps, 2, 5, 64, 1.0, fake, None, None) == -1
+    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, None, None, None) == -1
+    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake + 4, None, None) == -2
+    bad = (vp * 2)(fake, fake + 2)
+    assert lib.zero_shard_reduce(bad, 2, 1, 64, 1.0, fake, None, None) == -2
+    assert lib.zero_shard_reduce(reps, 2, 1, 1 << 32, 1.0, None, fake, None) == -3
+    assert lib.zero_shard_reduce(reps, 2, 1, 0, 1.0, fake, None, None) == 0
+    assert lib.zero_grad_norm(None, 1, 64, 1.0, fake, None) == -1
+    assert lib.zero_mxfp8_pack(fake, 33, fake, fake, None) == -3
+    assert lib.zero_mxfp8_pack(fake, 64, fake, fake + 1, None) == -2
+    assert lib.zero_mxfp8_pack(None, 64, fake, fake, None) == -1
+    assert lib.zero_mxfp8_pack(fake, 0, fake, fake, None) == 0
+    assert lib.zero_adamw_step(None, None) == -1
+    assert lib.zero_norm_acc_clear(None, 1, None) == -1
+    assert lib.zero_norm_acc_clear(fake + 8, 1, None) == -2
+    assert lib.zero_norm_acc_clear(None, 0, None) == 0

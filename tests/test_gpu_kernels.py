@@ -1,0 +1,304 @@
+"""Kernel-level parity of the HIP path against the CPU oracle, through the C
+ABI, at sizes that span several tiles plus ragged tails.  Bitwise throughout:
+reduction, norm accumulator, clip/skip gate, AdamW state, bf16 param and
+MXFP8 codes."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_util import (acc_from_oracle, from_dev, gpu_or_skip, mismatch_report, same_bits,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def zs():
+    gpu_or_skip()
+    import zero_sharded_mixed_step_amd as zs
+    zs.lib()
+    return zs
+
+
+def _replicas(P, n, bf16, seed, inject=()):
+    reps = []
+    for k in range(P):
+        sp = synth.make_spec(seed=seed, cfg=50, stream=1, step=1, replica=k, sigma=1e-3,
+                             outlier_rate=0.01, outlier_mult=100.0)
+        reps.append(synth.fill(sp, 0, n, bf16))
+    for (k, i, val) in inject:
+        if bf16:
+            reps[k][i] = O.f32_to_bf16(np.array([val], np.float32))[0]
+        else:
+            reps[k][i] = np.float32(val)
+    return reps
+
+
+# ------------------------------------------------------------- generator --
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_device_generator_matches_host(zs, bf16):
+    import torch
+    cases = [(0, 1), (0, 1000), (12345, 1 << 20), ((1 << 32) + 7, 4099)]
+    for start, count in cases:
+        sp = synth.make_spec(seed=3, cfg=9, stream=1, step=2, replica=5, sigma=1e-3,
+                             outlier_rate=0.01, outlier_mult=100.0, post_mul=65536.0)
+        t = torch.empty(count, dtype=torch.int16 if bf16 else torch.float32, device="cuda")
+        synth.fill_device(sp, start, t)
+        assert same_bits(from_dev(t, bf16), synth.fill(sp, start, count, bf16)), (start, count)
+
+
+# ---------------------------------------------------------------- reduce --
+
+SIZES = [1, 7, 8, 17, 31, 33, 1024, 4097, 65536 + 13]
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_shard_reduce_and_norm(zs, P, bf16):
+    import torch
+    for n in SIZES:
+        inject = [(P - 1, n - 1, np.inf)] if n > 5 else []
+        if n > 100:
+            inject += [(0, 3, np.nan), (P // 2, n // 2, -np.inf)]
+            if not bf16:
+                inject += [(0, 40, 2.0 ** 36)]    # finite, but its group overflows 2^64
+        reps = _replicas(P, n, bf16, seed=n, inject=inject)
+        inv = O.inv_scale(P, 1.0)
+        want_g = O.reduce(reps, inv)
+        want_acc = acc_from_oracle(O.norm_accumulate(want_g))
+        dreps = [to_dev(r) for r in reps]
+        g = torch.empty(n, dtype=torch.float32, device="cuda")
+        acc = zs.new_norm_acc(1)
+        zs.zero_shard_reduce(dreps, inv, g_out=g, acc=acc)
+        acc2 = zs.new_norm_acc(1)
+        zs.zero_shard_reduce(dreps, inv, acc=acc2)           # norm only
+        g2 = torch.empty(n, dtype=torch.float32, device="cuda")
+        zs.zero_shard_reduce(dreps, inv, g_out=g2)           # write only
+        torch.cuda.synchronize()
+        assert same_bits(from_dev(g), want_g), mismatch_report(f"g n={n}", from_dev(g), want_g)
+        assert same_bits(from_dev(g2), want_g), n
+        assert zs.read_norm_acc(acc)[0] == want_acc, (n, zs.read_norm_acc(acc)[0], want_acc)
+        assert zs.read_norm_acc(acc2)[0] == want_acc, n
+
+
+def test_grad_norm_with_loss_scale(zs):
+    import torch
+    for bf16 in (False, True):
+        for n in (31, 4096, 100003):
+            sp = synth.make_spec(seed=1, cfg=51, stream=1, sigma=1e-3, post_mul=65536.0)
+            x = synth.fill(sp, 0, n, bf16)
+            if bf16:
+                x[n // 3] = 0x7F80
+            inv = O.inv_scale(1, 65536.0)
+            want = acc_from_oracle(O.norm_accumulate(O.reduce([x], inv)))
+            acc = zs.new_norm_acc(1)
+            zs.zero_grad_norm(to_dev(x), inv, acc)
+            torch.cuda.synchronize()
+            assert zs.read_norm_acc(acc)[0] == want, (bf16, n)
+
+
+def test_buckets_and_grid_shapes_do_not_change_the_norm(zs):
+    import torch
+    P, n = 8, 32 * 50_001
+    reps = [to_dev(r) for r in _replicas(P, n, True, seed=7)]
+    inv = O.inv_scale(P, 1.0)
+    whole = zs.new_norm_acc(1)
+    zs.zero_shard_reduce(reps, inv, acc=whole)
+    for bucket in (32, 4096, 32 * 7919, 1 << 20):
+        acc = zs.new_norm_acc(1)
+        for lo in range(0, n, bucket):
+            hi = min(n, lo + bucket)
+            zs.zero_shard_reduce([r[lo:hi] for r in reps], inv, acc=acc)
+        torch.cuda.synchronize()
+        assert zs.read_norm_acc(acc) == zs.read_norm_acc(whole), bucket
+
+
+# ------------------------------------------------------------------ gate --
+
+def _acc_words(X, nonfinite, overflow, rng):
+    """Device layout of an accumulator holding X, with pending carries."""
+    d = [(X >> (32 * k)) & 0xFFFFFFFF for k in range(7)]
+    d[6] += (X >> 224) << 32 if X >> 224 else 0
+    for k in range(6, 0, -1):          # push some value down as pending carries
+        c = int(rng.integers(0, min(d[k], 1 << 31) + 1)) if d[k] else 0
+        d[k] -= c
+        d[k - 1] += c << 32
+    words = [v - (1 << 64) if v >= (1 << 63) else v for v in d]
+    tail = (overflow << 32) | nonfinite
+    words.append(tail - (1 << 64) if tail >= (1 << 63) else tail)
+    return words
+
+
+def test_gate_matches_oracle(zs):
+    import torch
+    rng = np.random.default_rng(21)
+    Xs = [0, 1, 3, (1 << 53) - 1, 1 << 53, (1 << 53) + 1, (1 << 54) + 2, (1 << 54) + 6,
+          25 << 128, (1 << 224) - 1]
+    for bits in range(1, 224, 2):
+        Xs.append(int(rng.integers(1, 1 << 62)) << max(0, bits - 62))
+    for m in ((1 << 52) + 1, (1 << 53) - 1):
+        for sh in (1, 60, 150):
+            Xs += [(2 * m + 1) << sh, ((2 * m + 1) << sh) + 1, ((2 * m + 1) << sh) - 1]
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
+    skip = torch.empty(1, dtype=torch.int32, device="cuda")
+    rows, expect = [], []
+    for X in Xs:
+        X &= (1 << 224) - 1
+        for max_norm in (1.0, 0.37, 1e6, 0.0):
+            for nonfinite, overflow, check in ((0, 0, 1), (2, 0, 1), (0, 1, 1), (3, 0, 0)):
+                parts = [X // 3, X // 3, X - 2 * (X // 3)]
+                words = []
+                oacc = O.acc_zero()
+                for j, part in enumerate(parts):
+                    nf = nonfinite if j == 0 else 0
+                    words.append(_acc_words(part, nf, overflow if j == 2 else 0, rng))
+                    a = O.acc_zero()
+                    for k in range(8):
+                        a.w[k] = (part >> (32 * k)) & 0xFFFFFFFF
+                    O.acc_add(oacc, a)
+                want_skip = int(check and (nonfinite + overflow) > 0)
+                want_coef = 1.0 if want_skip else O.clip_coef(O.acc_sumsq(oacc), max_norm)
+                rows.append((words, max_norm, check))
+                expect.append((want_coef, want_skip, X))
+    got = []
+    for words, max_norm, check in rows:
+        accs = torch.tensor(words, dtype=torch.int64, device="cuda")
+        zs.zero_step_gate(accs, max_norm, check, coef, skip)
+        got.append((coef.clone(), skip.clone()))
+    torch.cuda.synchronize()
+    for (c, s), (wc, ws, X) in zip(got, expect):
+        assert int(s.item()) == ws, hex(X)
+        if not ws:
+            assert np.float32(c.item()).view(np.uint32) == np.float32(wc).view(np.uint32), \
+                (hex(X), c.item(), wc)
+
+
+# ----------------------------------------------------------------- AdamW --
+
+HP = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (0.1, 0.5, 0.75, 1e-3, 0.5)]
+
+
+@pytest.mark.parametrize("source", ["grad_f32", "f32_P4", "bf16_P8", "bf16_P1", "bf16_P3"])
+@pytest.mark.parametrize("gated", [False, True])
+def test_adamw_multi_step(zs, source, gated):
+    import torch
+    for n in (17, 4096 + 5, 70001):
+        for hp in HP:
+            lr, b1, b2, eps, wd = hp
+            if source == "grad_f32":
+                P, bf16 = 1, False
+            else:
+                P, bf16 = int(source.split("_P")[1]), source.startswith("bf16")
+            ms = synth.make_spec(seed=n, cfg=52, stream=0, sigma=0.02)
+            master = synth.fill(ms, 0, n, False)
+            m = np.zeros(n, np.float32)
+            v = np.zeros(n, np.float32)
+            param = O.f32_to_bf16(master)
+            d = [to_dev(a) for a in (master, m, v, param)]
+            acc = zs.new_norm_acc(1)
+            skipped = torch.zeros(1, dtype=torch.int32, device="cuda")
+            max_norm = 0.05 if gated else 0.0
+            for t in range(1, 5):
+                reps = _replicas(P, n, bf16, seed=1000 * t + n)
+                inv = O.inv_scale(P, 1.0)
+                g = O.reduce(reps, inv)
+                coef = 1.0
+                if gated:
+                    coef = O.clip_coef(O.acc_sumsq(O.norm_accumulate(g)), max_norm)
+                O.adamw(g, coef, O.make_scalars(lr, b1, b2, eps, wd, t), master, m, v, param)
+                dreps = [to_dev(r) for r in reps]
+                kw = dict(step=t, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd,
+                          param_bf16=d[3])
+                if gated:
+                    zs.zero_norm_acc_clear(acc)
+                    zs.zero_shard_reduce(dreps, inv, acc=acc)
+                    kw.update(accs=acc, max_norm=max_norm, check_overflow=True,
+                              skipped_out=skipped)
+                if source == "grad_f32":
+                    zs.zero_adamw_step(d[0], d[1], d[2], grad_f32=to_dev(g), **kw)
+                else:
+                    zs.zero_adamw_step(d[0], d[1], d[2], replicas=dreps, inv_scale=inv, **kw)
+            torch.cuda.synchronize()
+            for name, got, want in zip(("master", "m", "v", "param"), d, (master, m, v, param)):
+                hg = from_dev(got, name == "param")
+                assert same_bits(hg, want), mismatch_report(f"{name} n={n} hp={hp}", hg, want)
+            if gated:
+                assert int(skipped.item()) == 0
+
+
+def test_adamw_skip_leaves_state_untouched(zs):
+    import torch
+    n, P = 4096 + 3, 4
+    reps = _replicas(P, n, True, seed=5, inject=[(2, n - 1, np.inf)])
+    ms = synth.make_spec(seed=5, cfg=53, stream=0, sigma=0.02)
+    master = synth.fill(ms, 0, n, False)
+    m = (master * np.float32(0.01)).astype(np.float32)
+    v = (master * master).astype(np.float32)
+    param = O.f32_to_bf16(master)
+    d = [to_dev(a) for a in (master, m, v, param)]
+    acc = zs.new_norm_acc(1)
+    skipped = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    dreps = [to_dev(r) for r in reps]
+    inv = O.inv_scale(P, 1.0)
+    zs.zero_shard_reduce(dreps, inv, acc=acc)
+    zs.zero_adamw_step(d[0], d[1], d[2], replicas=dreps, inv_scale=inv, step=3, lr=1e-3,
+                       weight_decay=0.01, param_bf16=d[3], accs=acc, max_norm=1.0,
+                       check_overflow=True, skipped_out=skipped)
+    torch.cuda.synchronize()
+    assert int(skipped.item()) == 1
+    assert zs.read_norm_acc(acc)[0][1] == 1
+    for got, want in zip(d, (master, m, v, param)):
+        assert same_bits(from_dev(got, want.dtype == np.uint16), want)
+
+
+# ----------------------------------------------------------------- MXFP8 --
+
+def test_mxfp8_all_patterns_and_blocks(zs):
+    import torch
+    rng = np.random.default_rng(31)
+    allpat = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    parts = [allpat, rng.permutation(allpat)]
+    finite = allpat[(allpat & 0x7F80) != 0x7F80]
+    parts.append(rng.permutation(finite)[: (finite.size // 32) * 32])
+    scaled = (rng.standard_normal(32 * 4096) * np.repeat(
+        np.exp2(rng.integers(-140, 128, size=4096)), 32)).astype(np.float32)
+    parts.append(O.f32_to_bf16(scaled))
+    blk = np.zeros(32 * 6, np.uint16)
+    blk[32 * 1 + 7] = 0x8000
+    blk[32 * 2] = 0x0001
+    blk[32 * 3:32 * 4] = 0x7F7F
+    blk[32 * 4 + 31] = 0xFF80
+    blk[32 * 5:32 * 6] = rng.integers(0, 1 << 16, 32)
+    parts.append(blk)
+    x = np.concatenate(parts)
+    for n in (x.size, 32, 32 * 5, 32 * 67):
+        xs = np.ascontiguousarray(x[:n])
+        want_e, want_s = O.mxfp8_pack(xs)
+        elem = torch.empty(n, dtype=torch.uint8, device="cuda")
+        scale = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+        zs.zero_mxfp8_pack(to_dev(xs), elem, scale)
+        torch.cuda.synchronize()
+        ge, gs = from_dev(elem), from_dev(scale)
+        assert np.array_equal(gs, want_s), (n, np.nonzero(gs != want_s)[0][:5])
+        assert np.array_equal(ge, want_e), (n, np.nonzero(ge != want_e)[0][:5])
+
+
+# ---------------------------------------------------------- determinism --
+
+def test_runs_are_bitwise_reproducible(zs):
+    import torch
+    n, P = 32 * 100_003, 8
+    dreps = [to_dev(r) for r in _replicas(P, n, True, seed=9)]
+    outs = []
+    for _ in range(2):
+        st = zs.ShardStep(n, P, torch.bfloat16, lr=1e-3, weight_decay=0.01, max_norm=1.0,
+                          check_overflow=True, bucket=32 * 10_000)
+        st.master.fill_(0.01)
+        st.step(dreps)
+        st.step(dreps)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().copy() for t in (st.master, st.m, st.v, st.param, st.acc)])
+    for a, b in zip(*outs):
+        assert same_bits(a, b)

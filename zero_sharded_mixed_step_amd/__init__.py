@@ -1,0 +1,13 @@
+"""One data-parallel rank's sharded mixed-precision optimizer step on MI355X.
+
+The kernels live in libzero_step.so (HIP, gfx950) behind the C ABI declared in
+include/zero_step.h; this package is its ctypes binding (`_binding`, same
+names as the C entry points) plus `ShardStep`, which sequences the calls of
+one step.  There is no host fallback: loading fails if the library is not
+built.
+"""
+from ._binding import (ZERO_BF16, ZERO_F32, ZERO_MAX_REPLICAS, ZeroStepError, lib,  # noqa: F401
+                       new_norm_acc, read_norm_acc, zero_abi_version, zero_adamw_step,
+                       zero_grad_norm, zero_inv_scale, zero_mxfp8_pack, zero_norm_acc_clear,
+                       zero_shard_reduce, zero_step_gate, zero_strerror)
+from .step import ShardStep  # noqa: F401

@@ -1,0 +1,228 @@
+"""ctypes binding of libzero_step.so, with the C entry points' names.
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and a nonzero status raises ZeroStepError.
+Every step of the computation runs in the library's HIP kernels; there is no
+host or fallback path.  PyTorch supplies device memory and streams.
+"""
+import ctypes as C
+import os
+
+import torch
+
+from . import build as _build
+
+ZERO_F32, ZERO_BF16 = 0, 1
+ZERO_MAX_REPLICAS = 64
+ACC_WORDS = 8          # one zero_norm_acc = 64 bytes = 8 int64 words
+
+_lib = None
+
+
+class ZeroStepError(RuntimeError):
+    def __init__(self, status, fn):
+        super().__init__(f"{fn}: {zero_strerror(status)} (status {status})")
+        self.status = status
+
+
+class _AdamArgs(C.Structure):
+    _fields_ = [("n", C.c_size_t), ("grad_f32", C.c_void_p), ("replicas", C.c_void_p),
+                ("P", C.c_int), ("dtype", C.c_int), ("inv_scale", C.c_float),
+                ("master", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p),
+                ("param_bf16", C.c_void_p), ("accs", C.c_void_p), ("n_accs", C.c_int),
+                ("max_norm", C.c_double), ("check_overflow", C.c_int),
+                ("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
+                ("skipped_out", C.c_void_p)]
+
+
+def lib():
+    """Load libzero_step.so; fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"{_build.LIB} is not built: run __graft_entry__.build() "
+                               "(there is no non-HIP implementation)")
+        L = C.CDLL(_build.LIB)
+        vp, sz, i = C.c_void_p, C.c_size_t, C.c_int
+        L.zero_abi_version.restype = i
+        L.zero_strerror.argtypes = [i]
+        L.zero_strerror.restype = C.c_char_p
+        L.zero_inv_scale.argtypes = [i, C.c_double]
+        L.zero_inv_scale.restype = C.c_float
+        L.zero_norm_acc_clear.argtypes = [vp, i, vp]
+        L.zero_shard_reduce.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp]
+        L.zero_grad_norm.argtypes = [vp, i, sz, C.c_float, vp, vp]
+        L.zero_adamw_step.argtypes = [C.POINTER(_AdamArgs), vp]
+        L.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
+        L.zero_mxfp8_pack.argtypes = [vp, sz, vp, vp, vp]
+        for f in (L.zero_norm_acc_clear, L.zero_shard_reduce, L.zero_grad_norm,
+                  L.zero_adamw_step, L.zero_step_gate, L.zero_mxfp8_pack):
+            f.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(status, fn):
+    if status != 0:
+        raise ZeroStepError(status, fn)
+
+
+def _stream(stream):
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return ZERO_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return ZERO_BF16
+    raise TypeError("replicas must be float32 or bf16 (bfloat16 / 16-bit bits)")
+
+
+def _ptr_array(tensors, name):
+    ptrs = [_dev_ptr(t, name).value for t in tensors]
+    return (C.c_void_p * len(ptrs))(*ptrs)
+
+
+def _acc_ptr(acc):
+    if acc is None:
+        return None, 0
+    if acc.dtype != torch.int64 or acc.numel() % ACC_WORDS:
+        raise TypeError("norm accumulators are int64 tensors of shape (k, 8)")
+    return _dev_ptr(acc, "acc"), acc.numel() // ACC_WORDS
+
+
+# ------------------------------------------------------------ helpers ---
+
+def zero_abi_version() -> int:
+    return lib().zero_abi_version()
+
+
+def zero_strerror(status: int) -> str:
+    return lib().zero_strerror(int(status)).decode()
+
+
+def zero_inv_scale(P: int, loss_scale: float = 1.0) -> float:
+    return lib().zero_inv_scale(int(P), float(loss_scale))
+
+
+def new_norm_acc(k: int = 1, device="cuda") -> torch.Tensor:
+    """k zeroed accumulators (64 bytes each) as an int64 (k, 8) tensor."""
+    acc = torch.empty((k, ACC_WORDS), dtype=torch.int64, device=device)
+    zero_norm_acc_clear(acc)
+    return acc
+
+
+def read_norm_acc(acc: torch.Tensor):
+    """Host view of accumulators: list of (X, nonfinite, overflow) with X the
+    integer whose value times 2^-128 is the sum of squares."""
+    words = acc.detach().reshape(-1, ACC_WORDS).cpu().tolist()
+    out = []
+    for w in words:
+        digits = [d & 0xFFFFFFFFFFFFFFFF for d in w[:7]]
+        tail = w[7] & 0xFFFFFFFFFFFFFFFF
+        X = sum(d << (32 * k) for k, d in enumerate(digits))
+        out.append((X, tail & 0xFFFFFFFF, tail >> 32))
+    return out
+
+
+# -------------------------------------------------------- entry points ---
+
+def zero_norm_acc_clear(accs: torch.Tensor, stream=None) -> None:
+    p, k = _acc_ptr(accs)
+    _check(lib().zero_norm_acc_clear(p, k, _stream(stream)), "zero_norm_acc_clear")
+
+
+def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
+                      stream=None) -> None:
+    reps = list(replicas)
+    if not reps:
+        raise ValueError("at least one replica")
+    n = reps[0].numel() if n is None else int(n)
+    for r in reps:
+        if r.numel() < n or r.dtype != reps[0].dtype:
+            raise ValueError("replicas must share dtype and hold n elements")
+    if g_out is not None and (g_out.dtype != torch.float32 or g_out.numel() < n):
+        raise ValueError("g_out must be float32 with n elements")
+    ap, k = _acc_ptr(acc)
+    if k > 1:
+        raise ValueError("zero_shard_reduce adds to one accumulator")
+    _check(lib().zero_shard_reduce(_ptr_array(reps, "replica"), len(reps), _dtype_code(reps[0]),
+                                   n, float(inv_scale), _dev_ptr(g_out, "g_out"), ap,
+                                   _stream(stream)), "zero_shard_reduce")
+
+
+def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:
+    n = grad.numel() if n is None else int(n)
+    ap, k = _acc_ptr(acc)
+    if k != 1:
+        raise ValueError("zero_grad_norm adds to one accumulator")
+    _check(lib().zero_grad_norm(_dev_ptr(grad, "grad"), _dtype_code(grad), n,
+                                float(inv_scale), ap, _stream(stream)), "zero_grad_norm")
+
+
+def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                    weight_decay=0.0, grad_f32=None, replicas=None, inv_scale=1.0,
+                    param_bf16=None, accs=None, max_norm=0.0, check_overflow=False,
+                    skipped_out=None, n=None, stream=None) -> None:
+    n = master.numel() if n is None else int(n)
+    for name, t in (("m", m), ("v", v)):
+        if t.numel() < n or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 with n elements")
+    if master.dtype != torch.float32:
+        raise ValueError("master must be float32")
+    a = _AdamArgs()
+    a.n = n
+    keep = None
+    if replicas is not None:
+        reps = list(replicas)
+        keep = _ptr_array(reps, "replica")
+        a.replicas = C.cast(keep, C.c_void_p)
+        a.P = len(reps)
+        a.dtype = _dtype_code(reps[0])
+    else:
+        a.P = 1
+        a.dtype = ZERO_F32
+    a.grad_f32 = _dev_ptr(grad_f32, "grad_f32")
+    a.inv_scale = float(inv_scale)
+    a.master, a.m, a.v = (_dev_ptr(master, "master"), _dev_ptr(m, "m"), _dev_ptr(v, "v"))
+    a.param_bf16 = _dev_ptr(param_bf16, "param_bf16")
+    a.accs, a.n_accs = _acc_ptr(accs)
+    a.max_norm = float(max_norm)
+    a.check_overflow = int(bool(check_overflow))
+    a.lr, a.beta1, a.beta2, a.eps, a.weight_decay = (float(lr), float(beta1), float(beta2),
+                                                      float(eps), float(weight_decay))
+    a.step = int(step)
+    a.skipped_out = _dev_ptr(skipped_out, "skipped_out")
+    rc = lib().zero_adamw_step(C.byref(a), _stream(stream))
+    del keep
+    _check(rc, "zero_adamw_step")
+
+
+def zero_step_gate(accs, max_norm, check_overflow, coef_out, skip_out, stream=None) -> None:
+    ap, k = _acc_ptr(accs)
+    _check(lib().zero_step_gate(ap, k, float(max_norm), int(bool(check_overflow)),
+                                _dev_ptr(coef_out, "coef_out"), _dev_ptr(skip_out, "skip_out"),
+                                _stream(stream)), "zero_step_gate")
+
+
+def zero_mxfp8_pack(x_bf16, elem_out, scale_out, n=None, stream=None) -> None:
+    n = x_bf16.numel() if n is None else int(n)
+    _check(lib().zero_mxfp8_pack(_dev_ptr(x_bf16, "x"), n, _dev_ptr(elem_out, "elem_out"),
+                                 _dev_ptr(scale_out, "scale_out"), _stream(stream)),
+           "zero_mxfp8_pack")

@@ -1,0 +1,199 @@
+// zs_abi.hip -- the extern "C" entry points of libzero_step.so: argument
+// checks, the per-step AdamW scalars (binary64, each rounded once to
+// binary32), and the launches.  No allocation, no synchronisation, and no
+// C++ exception crosses this boundary.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "zero_step.h"
+#include "zs_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int status_of(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_EHIP; }
+
+int check_replicas(const void* const* replicas, int P, int dtype) {
+  if (replicas == nullptr || P < 1 || P > ZERO_MAX_REPLICAS) return ZERO_EINVAL;
+  if (dtype != ZERO_F32 && dtype != ZERO_BF16) return ZERO_EINVAL;
+  for (int k = 0; k < P; ++k) {
+    if (replicas[k] == nullptr) return ZERO_EINVAL;
+    if (!aligned16(replicas[k])) return ZERO_EALIGN;
+  }
+  return ZERO_OK;
+}
+
+// beta^t by square-and-multiply over the bits of t, least significant bit
+// first, in binary64 (the fixed evaluation order the step's scalars use).
+double power_lsb_first(double beta, int64_t t) {
+  double acc = 1.0;
+  double sq = beta;
+  for (uint64_t e = static_cast<uint64_t>(t); e != 0; e >>= 1) {
+    if (e & 1u) acc = acc * sq;
+    sq = sq * sq;
+  }
+  return acc;
+}
+
+zs::AdamScalars derive_scalars(double lr, double beta1, double beta2, double eps, double wd,
+                               int64_t t) {
+  zs::AdamScalars s;
+  s.b1 = static_cast<float>(beta1);
+  s.b2 = static_cast<float>(beta2);
+  s.omb1 = static_cast<float>(1.0 - beta1);
+  s.omb2 = static_cast<float>(1.0 - beta2);
+  const double bias1 = 1.0 - power_lsb_first(beta1, t);
+  const double bias2 = 1.0 - power_lsb_first(beta2, t);
+  s.step_size = static_cast<float>(lr / bias1);
+  s.sqrt_bc2 = static_cast<float>(std::sqrt(bias2));
+  const double lw = lr * wd;
+  s.decay = static_cast<float>(1.0 - lw);
+  s.eps = static_cast<float>(eps);
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_abi_version(void) { return ZERO_ABI_VERSION; }
+
+const char* zero_strerror(int status) {
+  switch (status) {
+    case ZERO_OK: return "ok";
+    case ZERO_EINVAL: return "invalid argument (null pointer, replica count, dtype, step or "
+                             "gradient source)";
+    case ZERO_EALIGN: return "device pointer not 16-byte aligned";
+    case ZERO_ESIZE: return "size not supported (MXFP8 needs n % 32 == 0; a norm call needs "
+                            "n < 2^32)";
+    case ZERO_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+float zero_inv_scale(int P, double loss_scale) {
+  const double denom = static_cast<double>(P) * loss_scale;
+  return static_cast<float>(1.0 / denom);
+}
+
+int zero_norm_acc_clear(zero_norm_acc* accs, int n_accs, void* stream) {
+  try {
+    if (n_accs < 0) return ZERO_EINVAL;
+    if (n_accs == 0) return ZERO_OK;
+    if (accs == nullptr) return ZERO_EINVAL;
+    if (!aligned16(accs)) return ZERO_EALIGN;
+    return status_of(zs::launch_acc_clear(accs, n_accs, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, float inv_scale,
+                      float* g_out, zero_norm_acc* acc, void* stream) {
+  try {
+    const int rc = check_replicas(replicas, P, dtype);
+    if (rc != ZERO_OK) return rc;
+    if (g_out == nullptr && acc == nullptr) return ZERO_EINVAL;
+    if ((g_out && !aligned16(g_out)) || (acc && !aligned16(acc))) return ZERO_EALIGN;
+    if (acc != nullptr && n >= (size_t(1) << 32)) return ZERO_ESIZE;
+    if (n == 0) return ZERO_OK;
+    return status_of(
+        zs::launch_reduce(replicas, P, dtype, n, inv_scale, g_out, acc, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+int zero_grad_norm(const void* grad, int dtype, size_t n, float inv_scale, zero_norm_acc* acc,
+                   void* stream) {
+  try {
+    if (grad == nullptr || acc == nullptr) return ZERO_EINVAL;
+    const void* reps[1] = {grad};
+    const int rc = check_replicas(reps, 1, dtype);
+    if (rc != ZERO_OK) return rc;
+    if (!aligned16(acc)) return ZERO_EALIGN;
+    if (n >= (size_t(1) << 32)) return ZERO_ESIZE;
+    if (n == 0) return ZERO_OK;
+    return status_of(
+        zs::launch_reduce(reps, 1, dtype, n, inv_scale, nullptr, acc, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+int zero_adamw_step(const zero_adamw_args* a, void* stream) {
+  try {
+    if (a == nullptr) return ZERO_EINVAL;
+    if (a->master == nullptr || a->m == nullptr || a->v == nullptr) return ZERO_EINVAL;
+    if ((a->grad_f32 == nullptr) == (a->replicas == nullptr)) return ZERO_EINVAL;
+    if (a->step < 1 || a->n_accs < 0 || (a->n_accs > 0 && a->accs == nullptr))
+      return ZERO_EINVAL;
+    if (a->replicas != nullptr) {
+      const int rc = check_replicas(a->replicas, a->P, a->dtype);
+      if (rc != ZERO_OK) return rc;
+    }
+    if (!aligned16(a->master) || !aligned16(a->m) || !aligned16(a->v) ||
+        (a->grad_f32 && !aligned16(a->grad_f32)) ||
+        (a->param_bf16 && !aligned16(a->param_bf16)) || (a->accs && !aligned16(a->accs)) ||
+        (a->skipped_out && !aligned4(a->skipped_out)))
+      return ZERO_EALIGN;
+    zs::AdamLaunch L;
+    L.grad = a->grad_f32;
+    L.replicas = a->replicas;
+    L.P = a->replicas ? a->P : 1;
+    L.dtype = a->dtype;
+    L.inv_scale = a->inv_scale;
+    L.master = a->master;
+    L.m = a->m;
+    L.v = a->v;
+    L.param = a->param_bf16;
+    L.accs = a->n_accs > 0 ? a->accs : nullptr;
+    L.n_accs = a->n_accs;
+    L.max_norm = a->max_norm;
+    L.check_overflow = a->check_overflow;
+    L.skipped_out = a->skipped_out;
+    L.n = a->n;
+    L.s = derive_scalars(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
+    if (a->n == 0 && a->skipped_out == nullptr) return ZERO_OK;
+    return status_of(zs::launch_adamw(L, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+int zero_step_gate(const zero_norm_acc* accs, int n_accs, double max_norm, int check_overflow,
+                   float* coef_out, int32_t* skip_out, void* stream) {
+  try {
+    if (coef_out == nullptr || skip_out == nullptr || n_accs < 0 ||
+        (n_accs > 0 && accs == nullptr))
+      return ZERO_EINVAL;
+    if ((accs && !aligned16(accs)) || !aligned4(coef_out) || !aligned4(skip_out))
+      return ZERO_EALIGN;
+    return status_of(zs::launch_gate(n_accs > 0 ? accs : nullptr, n_accs, max_norm,
+                                     check_overflow, coef_out, skip_out, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+int zero_mxfp8_pack(const uint16_t* bf16_in, size_t n, uint8_t* elem_out, uint8_t* scale_out,
+                    void* stream) {
+  try {
+    if (n % 32 != 0) return ZERO_ESIZE;
+    if (n == 0) return ZERO_OK;
+    if (bf16_in == nullptr || elem_out == nullptr || scale_out == nullptr) return ZERO_EINVAL;
+    if (!aligned16(bf16_in) || !aligned16(elem_out) || !aligned16(scale_out))
+      return ZERO_EALIGN;
+    return status_of(zs::launch_mxfp8(bf16_in, n, elem_out, scale_out, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+}  // extern "C"

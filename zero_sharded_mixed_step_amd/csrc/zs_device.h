@@ -1,0 +1,299 @@
+// zs_device.h -- device building blocks shared by the step's kernels:
+// vector loads of gradient replicas, the fixed-order shard reduce, the exact
+// fixed-point sum of squares, and the on-device clip/skip gate.
+//
+// Data layout: every array is a flat, 16-byte aligned vector.  A lane works
+// on a "chunk" of 8 consecutive elements (one 16-byte load of bf16, two of
+// fp32).  Four consecutive chunks, held by four consecutive lanes of one
+// wavefront, form a 32-element norm group, so the group sum
+// (a0 + a1) + (a2 + a3) is two quad-permute DPP steps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_step.h"
+
+namespace zs {
+
+constexpr int kThreads = 256;  // four wave64 wavefronts per workgroup
+constexpr int kVec = 8;        // elements per chunk
+
+struct Replicas {
+  const void* p[ZERO_MAX_REPLICAS];
+};
+
+// ------------------------------------------------------------- loads ------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Eight elements of one replica as fp32 (bf16 widening is exact).  `full`
+// is false only for the final, partial chunk: its elements past `n` read as
+// +0 and nothing beyond the buffer is touched.
+template <int DT>
+__device__ __forceinline__ void load_chunk(const void* base, uint64_t c, bool full,
+                                           uint64_t n, float x[kVec]) {
+  const uint64_t e0 = c * kVec;
+  if (DT == ZERO_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + e0;
+    if (full) {
+      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(ws[j] << 16);
+        x[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) x[j] = (e0 + j < n) ? bf16_bits_to_f32(p[j]) : 0.0f;
+    }
+  } else {
+    const float* p = static_cast<const float*>(base) + e0;
+    if (full) {
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) x[j] = (e0 + j < n) ? p[j] : 0.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ void load_f32_chunk(const float* base, uint64_t c, bool full,
+                                               uint64_t n, float x[kVec]) {
+  load_chunk<ZERO_F32>(base, c, full, n, x);
+}
+
+__device__ __forceinline__ void store_f32_chunk(float* base, uint64_t c, bool full,
+                                                uint64_t n, const float x[kVec]) {
+  float* p = base + c * kVec;
+  if (full) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+    const uint64_t e0 = c * kVec;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j)
+      if (e0 + j < n) p[j] = x[j];
+  }
+}
+
+// ------------------------------------------------------------ reduce ------
+
+// g = (r_0 + r_1 + ... + r_{P-1}) * inv_scale in binary32, rank order.
+// PT > 0 fixes P at compile time (all P loads issue before the adds);
+// PT == 0 reads the runtime count.
+template <int DT, int PT>
+__device__ __forceinline__ void reduce_chunk(const Replicas& R, int P, uint64_t c, bool full,
+                                             uint64_t n, float inv_scale, float g[kVec]) {
+  if constexpr (PT > 0) {
+    float x[PT][kVec];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) load_chunk<DT>(R.p[k], c, full, n, x[k]);
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      float s = x[0][j];
+#pragma unroll
+      for (int k = 1; k < PT; ++k) s = s + x[k][j];
+      g[j] = s * inv_scale;
+    }
+  } else {
+    float s[kVec];
+    load_chunk<DT>(R.p[0], c, full, n, s);
+    for (int k = 1; k < P; ++k) {
+      float x[kVec];
+      load_chunk<DT>(R.p[k], c, full, n, x);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) g[j] = s[j] * inv_scale;
+  }
+}
+
+// -------------------------------------------------- exact sum of squares --
+
+// a = q_0 + q_1 + ... + q_7 left to right in binary64 with q_j = g_j^2
+// (exact, so fma(g, g, a) rounds exactly like a + q).  Non-finite values
+// add 0 and are counted.
+__device__ __forceinline__ double chunk_sumsq(const float g[kVec], uint32_t& nonfinite) {
+  double a = 0.0;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const bool fin = __builtin_isfinite(g[j]);
+    nonfinite += fin ? 0u : 1u;
+    const double xd = fin ? static_cast<double>(g[j]) : 0.0;
+    a = __builtin_fma(xd, xd, a);
+  }
+  return a;
+}
+
+__device__ __forceinline__ double dpp_quad_perm(double x, int ctrl_tag) {
+  // ctrl_tag 1: lanes (1,0,3,2) of each quad; 2: lanes (2,3,0,1).
+  const uint64_t b = __double_as_longlong(x);
+  int lo = static_cast<int>(b & 0xFFFFFFFFu);
+  int hi = static_cast<int>(b >> 32);
+  if (ctrl_tag == 1) {
+    lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+    hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false);
+  } else {
+    lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+    hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false);
+  }
+  return __longlong_as_double((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                              static_cast<uint32_t>(lo));
+}
+
+// Group sum S = (a0 + a1) + (a2 + a3) over the quad; every lane of the quad
+// ends with the same S (IEEE addition is commutative).  Must be reached by
+// all 64 lanes.
+__device__ __forceinline__ double quad_group_sum(double a) {
+  const double b = a + dpp_quad_perm(a, 1);
+  return b + dpp_quad_perm(b, 2);
+}
+
+// floor(S * 2^128) split into three 32-bit pieces at digits base, base+1,
+// base+2 (S >= 0 finite, S < 2^64).  Lane q of the quad (0..2) returns
+// piece q and its digit; lane 3 returns 0.
+__device__ __forceinline__ void fixed_point_piece(double S, int quad_lane, int& digit,
+                                                  uint64_t& piece) {
+  const uint64_t bits = __double_as_longlong(S);
+  const int ex = static_cast<int>((bits >> 52) & 0x7FF);
+  piece = 0;
+  digit = 0;
+  if (ex == 0 || ex >= 1087) return;  // zero/subnormal (< 2^-1022) or >= 2^64
+  const uint64_t mant = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  const int sh = ex - 947;  // S * 2^128 = mant * 2^sh
+  uint32_t p0, p1, p2;
+  int base;
+  if (sh < 0) {
+    const uint64_t v = (sh <= -53) ? 0ull : (mant >> (-sh));
+    p0 = static_cast<uint32_t>(v);
+    p1 = static_cast<uint32_t>(v >> 32);
+    p2 = 0u;
+    base = 0;
+  } else {
+    const int r = sh & 31;
+    base = sh >> 5;
+    const uint64_t lo = mant << r;
+    const uint64_t hi = r ? (mant >> (64 - r)) : 0ull;
+    p0 = static_cast<uint32_t>(lo);
+    p1 = static_cast<uint32_t>(lo >> 32);
+    p2 = static_cast<uint32_t>(hi);
+  }
+  const uint32_t mine = quad_lane == 0 ? p0 : (quad_lane == 1 ? p1 : (quad_lane == 2 ? p2 : 0u));
+  piece = mine;
+  digit = base + (quad_lane < 3 ? quad_lane : 0);
+}
+
+// ----------------------------------------------------------- the gate ----
+
+struct Gate {
+  float coef;
+  int32_t skip;
+};
+
+// Sum of the accumulators as a normalised 256-bit integer (8 x 32 bits).
+__device__ inline void acc_total(const zero_norm_acc* accs, int n_accs, uint32_t w[8],
+                                 uint64_t& nonfinite, uint64_t& overflow) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = 0u;
+  nonfinite = 0;
+  overflow = 0;
+  for (int a = 0; a < n_accs; ++a) {
+    uint32_t t[8];
+    uint64_t carry = 0;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      const uint64_t x = accs[a].digit[k];
+      const uint64_t s = (x & 0xFFFFFFFFull) + carry;
+      t[k] = static_cast<uint32_t>(s);
+      carry = (x >> 32) + (s >> 32);
+    }
+    t[7] = static_cast<uint32_t>(carry);
+    uint64_t c2 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t s = static_cast<uint64_t>(w[k]) + t[k] + c2;
+      w[k] = static_cast<uint32_t>(s);
+      c2 = s >> 32;
+    }
+    nonfinite += accs[a].nonfinite;
+    overflow += accs[a].overflow;
+  }
+}
+
+// RNE_binary64(X * 2^-128) for X held in w[0..7].
+__device__ inline double fixed_to_double(const uint32_t w[8]) {
+  int top_word = -1;
+#pragma unroll
+  for (int k = 7; k >= 0; --k)
+    if (top_word < 0 && w[k] != 0u) top_word = k;
+  if (top_word < 0) return 0.0;
+  const int top = 32 * top_word + (31 - __clz(static_cast<int>(w[top_word])));
+  // bit(pos) of the 256-bit number
+  auto bit = [&](int pos) -> uint32_t {
+    return pos < 0 ? 0u : ((w[pos >> 5] >> (pos & 31)) & 1u);
+  };
+  uint64_t mant = 0;
+  int exp2;
+  if (top <= 52) {
+    // exact: X < 2^53
+    mant = (static_cast<uint64_t>(w[1]) << 32) | w[0];
+    exp2 = 0;
+  } else {
+    const int s = top - 52;  // lowest kept bit
+    // bits [s, s+52] via a funnel over three words
+    const int i = s >> 5, off = s & 31;
+    const uint64_t lo = (static_cast<uint64_t>(w[i + 1]) << 32) | w[i];
+    const uint64_t hi = (i + 2 < 8) ? w[i + 2] : 0u;
+    mant = off ? ((lo >> off) | (hi << (64 - off))) : lo;
+    mant &= (1ull << 53) - 1ull;
+    const uint32_t round_bit = bit(s - 1);
+    uint32_t sticky = 0;
+    // everything below s-1
+    const int below = s - 1;  // number of bits under the rounding bit
+    for (int k = 0; k < 8 && 32 * k < below; ++k) {
+      const int hi_bits = below - 32 * k;  // bits of word k that are below
+      const uint32_t mask = hi_bits >= 32 ? 0xFFFFFFFFu : ((1u << hi_bits) - 1u);
+      sticky |= (w[k] & mask);
+    }
+    exp2 = s;
+    if (round_bit && (sticky != 0u || (mant & 1ull))) {
+      mant += 1;
+      if (mant == (1ull << 53)) {
+        mant >>= 1;
+        exp2 += 1;
+      }
+    }
+  }
+  return __builtin_amdgcn_ldexp(static_cast<double>(mant), exp2 - 128);
+}
+
+__device__ inline Gate evaluate_gate(const zero_norm_acc* accs, int n_accs, double max_norm,
+                                     int check_overflow) {
+  Gate g{1.0f, 0};
+  if (n_accs <= 0 || accs == nullptr) return g;
+  uint32_t w[8];
+  uint64_t nonfinite, overflow;
+  acc_total(accs, n_accs, w, nonfinite, overflow);
+  if (check_overflow && (nonfinite + overflow) > 0) {
+    g.skip = 1;
+    return g;
+  }
+  if (max_norm > 0.0) {
+    const double sumsq = fixed_to_double(w);
+    const double norm = __builtin_sqrt(sumsq);
+    const double denom = norm + 1e-6;
+    const double c = max_norm / denom;
+    g.coef = (c < 1.0) ? static_cast<float>(c) : 1.0f;
+  }
+  return g;
+}
+
+}  // namespace zs

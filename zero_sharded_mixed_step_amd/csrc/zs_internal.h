@@ -1,0 +1,58 @@
+// zs_internal.h -- launchers between the C ABI (zs_abi.hip) and the kernels
+// (zs_kernels.hip).  Arguments arrive validated; launchers only pick the
+// template instance and the grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_step.h"
+
+namespace zs {
+
+struct AdamScalars {
+  float b1, b2, omb1, omb2, step_size, sqrt_bc2, decay, eps;
+};
+
+// Workgroups per compute unit of the persistent grids (a build-time knob).
+#ifndef ZS_BLOCKS_PER_CU
+#define ZS_BLOCKS_PER_CU 4
+#endif
+
+int compute_units(int device);
+
+hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t n,
+                         float inv_scale, float* g_out, zero_norm_acc* acc,
+                         hipStream_t stream);
+
+struct AdamLaunch {
+  const float* grad;
+  const void* const* replicas;
+  int P;
+  int dtype;
+  float inv_scale;
+  float* master;
+  float* m;
+  float* v;
+  uint16_t* param;
+  const zero_norm_acc* accs;
+  int n_accs;
+  double max_norm;
+  int check_overflow;
+  int32_t* skipped_out;
+  uint64_t n;
+  AdamScalars s;
+};
+
+hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream);
+
+hipError_t launch_gate(const zero_norm_acc* accs, int n_accs, double max_norm,
+                       int check_overflow, float* coef_out, int32_t* skip_out,
+                       hipStream_t stream);
+
+hipError_t launch_acc_clear(zero_norm_acc* accs, int n_accs, hipStream_t stream);
+
+hipError_t launch_mxfp8(const uint16_t* in, uint64_t n, uint8_t* elem, uint8_t* scale,
+                        hipStream_t stream);
+
+}  // namespace zs

@@ -1,0 +1,153 @@
+"""Sequencing of one rank's optimizer step over the C-ABI calls.
+
+`ShardStep` owns the rank's state buffers (fp32 master/m/v, bf16 param,
+optional fp32 gradient, the norm accumulator, the skip flag, MXFP8 output)
+and issues, on the current stream, the kernel launches of one step.  It
+computes nothing itself.
+
+Pass structure (bytes per shard element; g_b = bytes per replica element):
+  - no gate (no clip, no overflow check): one fused pass, AdamW reads the P
+    replicas directly: P*g_b + 26 bytes;
+  - gated: the update waits for the global norm / overflow state, so either
+    materialise:  reduce writes fp32 g (+4) and AdamW re-reads it (+4), or
+    recompute:    a norm-only pass over the replicas, then AdamW reduces the
+                  replicas again (+P*g_b);
+    whichever moves fewer bytes (materialise when P*g_b > 8).
+The reduce runs bucket by bucket when `bucket` is set; the norm state of all
+buckets accumulates in one accumulator (integer sums, so bucketing changes no
+bit of the result).
+
+Step counter: `t` counts applied updates.  With the overflow check on, the
+device decides the skip; the flag travels to pinned host memory behind an
+event and is read just before the next step's AdamW launch, after that
+step's reduce work is already queued, so the GPU never waits on the host.
+"""
+from typing import List, Optional
+
+import torch
+
+from . import _binding as B
+
+
+class ShardStep:
+    def __init__(self, n: int, P: int, grad_dtype: torch.dtype, *, lr: float,
+                 beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                 weight_decay: float = 0.0, max_norm: float = 0.0,
+                 check_overflow: bool = False, loss_scale: float = 1.0,
+                 bucket: Optional[int] = None, pack: bool = False,
+                 path: Optional[str] = None, device="cuda"):
+        self.n, self.P = int(n), int(P)
+        self.lr, self.beta1, self.beta2, self.eps, self.wd = lr, beta1, beta2, eps, weight_decay
+        self.max_norm, self.check_overflow = float(max_norm), bool(check_overflow)
+        self.inv_scale = B.zero_inv_scale(P, loss_scale)
+        self.bucket = int(bucket) if bucket else None
+        if self.bucket is not None and self.bucket % 32:
+            raise ValueError("buckets must be multiples of 32 elements")
+        g_b = 4 if grad_dtype == torch.float32 else 2
+        if path is None:
+            if not self.gated:
+                path = "fused"
+            else:
+                path = "materialize" if self.P * g_b > 8 else "recompute"
+        if path not in ("fused", "materialize", "recompute"):
+            raise ValueError(path)
+        if path == "fused" and self.gated:
+            raise ValueError("a gated step needs the norm before the update")
+        self.path = path
+        dev = torch.device(device)
+        self.master = torch.empty(self.n, dtype=torch.float32, device=dev)
+        self.m = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.param = torch.empty(self.n, dtype=torch.int16, device=dev)   # bf16 bits
+        self.g = (torch.empty(self.n, dtype=torch.float32, device=dev)
+                  if path == "materialize" else None)
+        self.acc = B.new_norm_acc(1, dev)
+        self.skipped = torch.zeros(1, dtype=torch.int32, device=dev)
+        self._skip_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+        self._skip_event = None
+        self.t = 0
+        self.pack = pack
+        if pack:
+            if self.n % 32:
+                raise ValueError("MXFP8 packing needs n % 32 == 0")
+            self.mx_elem = torch.empty(self.n, dtype=torch.uint8, device=dev)
+            self.mx_scale = torch.empty(self.n // 32, dtype=torch.uint8, device=dev)
+
+    @property
+    def gated(self) -> bool:
+        return self.max_norm > 0 or self.check_overflow
+
+    def bytes_per_element(self, g_b: int) -> int:
+        """Fused-minimum HBM bytes per shard element of this step's passes."""
+        fixed = 26
+        if self.path == "fused":
+            return self.P * g_b + fixed
+        if self.path == "materialize":
+            return self.P * g_b + 8 + fixed
+        return 2 * self.P * g_b + fixed
+
+    def _ranges(self):
+        if self.bucket is None:
+            yield 0, self.n
+        else:
+            for lo in range(0, self.n, self.bucket):
+                yield lo, min(self.n, lo + self.bucket)
+
+    def reduce(self, replicas: List[torch.Tensor]) -> None:
+        """Clear the accumulator and run the reduce/norm pass(es)."""
+        B.zero_norm_acc_clear(self.acc)
+        if self.path == "fused":
+            return
+        for lo, hi in self._ranges():
+            views = [r[lo:hi] for r in replicas]
+            if self.path == "materialize":
+                B.zero_shard_reduce(views, self.inv_scale, g_out=self.g[lo:hi], acc=self.acc)
+            else:
+                B.zero_shard_reduce(views, self.inv_scale, acc=self.acc)
+
+    def _resolve_pending_skip(self) -> None:
+        if self._skip_event is not None:
+            self._skip_event.synchronize()
+            self._skip_event = None
+            if int(self._skip_host[0]) == 0:
+                self.t += 1
+
+    def update(self, replicas: Optional[List[torch.Tensor]] = None,
+               accs: Optional[torch.Tensor] = None) -> None:
+        """AdamW on the shard; `accs` (k, 8) replaces the own accumulator when
+        the global norm state includes other ranks."""
+        self._resolve_pending_skip()
+        kw = dict(step=self.t + 1, lr=self.lr, beta1=self.beta1, beta2=self.beta2,
+                  eps=self.eps, weight_decay=self.wd, param_bf16=self.param,
+                  max_norm=self.max_norm, check_overflow=self.check_overflow)
+        if self.gated:
+            kw["accs"] = self.acc if accs is None else accs
+        if self.check_overflow:
+            kw["skipped_out"] = self.skipped
+        if self.path == "materialize":
+            B.zero_adamw_step(self.master, self.m, self.v, grad_f32=self.g, **kw)
+        else:
+            B.zero_adamw_step(self.master, self.m, self.v, replicas=replicas,
+                              inv_scale=self.inv_scale, **kw)
+        if self.check_overflow:
+            self._skip_host.copy_(self.skipped, non_blocking=True)
+            self._skip_event = torch.cuda.Event()
+            self._skip_event.record()
+        else:
+            self.t += 1
+
+    def pack_param(self) -> None:
+        B.zero_mxfp8_pack(self.param, self.mx_elem, self.mx_scale)
+
+    def step(self, replicas: List[torch.Tensor], accs: Optional[torch.Tensor] = None) -> None:
+        """One whole step: reduce (+ norm), gated AdamW, bf16 param, and the
+        MXFP8 pack of the param shard when enabled."""
+        self.reduce(replicas)
+        self.update(replicas, accs)
+        if self.pack:
+            self.pack_param()
+
+    def applied_steps(self) -> int:
+        """Applied updates so far (waits for the last skip flag)."""
+        self._resolve_pending_skip()
+        return self.t
