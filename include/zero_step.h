@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ZERO_ABI_VERSION 1
+#define ZERO_ABI_VERSION 2
 #define ZERO_MAX_REPLICAS 64
 
 /* Element types of gradient replicas. */
@@ -143,6 +143,8 @@ typedef struct zero_adamw_args {
   double lr, beta1, beta2, eps, weight_decay;
   int64_t step;                /* 1-based index of this applied update      */
   int32_t *skipped_out;        /* device int: 1 skipped, 0 applied; or NULL */
+  uint8_t *mx_elem_out;        /* uint8[n]: MXFP8 codes of the new params,  */
+  uint8_t *mx_scale_out;       /* uint8[n/32]: their scales; both or NULL   */
 } zero_adamw_args;
 
 /* Fused AdamW step on n elements of fp32 master/m/v.
@@ -163,7 +165,11 @@ typedef struct zero_adamw_args {
  *   d = sqrt(v) / sqrt_bc2 + eps; u = m / d
  *   master = fma(-step_size, u, master * decay); param = bf16_rne(master)
  * where g comes from grad_f32, or from the replicas exactly as
- * zero_shard_reduce computes it.  NaN params become 0x7FC0 with the sign. */
+ * zero_shard_reduce computes it.  NaN params become 0x7FC0 with the sign.
+ * With mx_elem_out/mx_scale_out set (n % 32 == 0, else ZERO_ESIZE) the same
+ * pass also writes the MXFP8 pack of the new bf16 params, bit for bit what
+ * zero_mxfp8_pack would produce from param_bf16, without reading it back.
+ * A skipped step writes none of the outputs. */
 int zero_adamw_step(const zero_adamw_args *args, void *stream);
 
 /* The gate alone, for inspection: writes *coef_out (device float) and

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.zero_abi_version.restype = C.c_int
-    assert lib.zero_abi_version() == 1
+    assert lib.zero_abi_version() == 2
     lib.zero_strerror.restype = C.c_char_p
     lib.zero_strerror.argtypes = [C.c_int]
     texts = {lib.zero_strerror(s).decode() for s in (0, -1, -2, -3, -4, 7)}

@@ -237,12 +237,15 @@ def test_30b_shard_clip_overflow_then_mxfp8(zs):
     blocks = np.unique(rng.integers(0, w.S // 32, size=256))
     blocks = np.unique(np.concatenate([blocks, [0, w.S // 32 - 1]]))
     eidx = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel().astype(np.uint64)
-    st.pack_param()
-    torch.cuda.synchronize()
     de = torch.from_numpy(eidx.astype(np.int64)).cuda()
     ds = torch.from_numpy(blocks.astype(np.int64)).cuda()
+    assert st.fuse_pack
+    fused_e, fused_s = from_dev(st.mx_elem[de]), from_dev(st.mx_scale[ds])
+    st.pack_param()                       # the standalone pack kernel
+    torch.cuda.synchronize()
     got_e, got_s = from_dev(st.mx_elem[de]), from_dev(st.mx_scale[ds])
     _, _, _, param, _ = _oracle_samples(w, eidx, range(1, 3), gates)
     want_e, want_s = O.mxfp8_pack(param)
-    assert np.array_equal(got_s, want_s)
-    assert np.array_equal(got_e, want_e)
+    for e, sc in ((fused_e, fused_s), (got_e, got_s)):
+        assert np.array_equal(sc, want_s)
+        assert np.array_equal(e, want_e)

@@ -228,6 +228,34 @@ def test_adamw_multi_step(zs, source, gated):
                 assert int(skipped.item()) == 0
 
 
+def test_adamw_fused_mxfp8_epilogue(zs):
+    import torch
+    for n, P, bf16 in ((32, 1, True), (4096 + 32, 8, True), (32 * 30011, 4, False)):
+        ms = synth.make_spec(seed=n, cfg=54, stream=0, sigma=0.02)
+        master = synth.fill(ms, 0, n, False)
+        master[5] = np.float32(3.0e38)            # a huge value (block saturates/overflows)
+        if n > 64:
+            master[40:72] = 0.0                   # an all-zero block before the update
+        m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        param = O.f32_to_bf16(master)
+        d = [to_dev(a) for a in (master, m, v, param)]
+        elem = torch.empty(n, dtype=torch.uint8, device="cuda")
+        scale = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+        for t in (1, 2, 3):
+            reps = _replicas(P, n, bf16, seed=77 * t + n)
+            inv = O.inv_scale(P, 1.0)
+            O.adamw(O.reduce(reps, inv), 1.0, O.make_scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, t),
+                    master, m, v, param)
+            zs.zero_adamw_step(d[0], d[1], d[2], replicas=[to_dev(r) for r in reps],
+                               inv_scale=inv, step=t, lr=1e-3, weight_decay=0.01,
+                               param_bf16=d[3], mx_elem_out=elem, mx_scale_out=scale)
+        torch.cuda.synchronize()
+        want_e, want_s = O.mxfp8_pack(param)
+        assert same_bits(from_dev(d[3], True), param)
+        assert np.array_equal(from_dev(scale), want_s), n
+        assert np.array_equal(from_dev(elem), want_e), n
+
+
 def test_adamw_skip_leaves_state_untouched(zs):
     import torch
     n, P = 4096 + 3, 4
@@ -283,6 +311,45 @@ def test_mxfp8_all_patterns_and_blocks(zs):
         ge, gs = from_dev(elem), from_dev(scale)
         assert np.array_equal(gs, want_s), (n, np.nonzero(gs != want_s)[0][:5])
         assert np.array_equal(ge, want_e), (n, np.nonzero(ge != want_e)[0][:5])
+
+
+def _reachable_blocks():
+    """For every scale exponent e_s in [-127, 119]: blocks of one anchor
+    element 2^(e_s + 8) (which sets e_s) and 31 of the bf16 values that can
+    share a block with it (|x| < 2^(e_s + 9)), both signs, all of them."""
+    mags = np.arange(0x7F80, dtype=np.int64)          # finite bf16 magnitudes
+    out = []
+    for e_s in range(-127, 120):
+        E = e_s + 8
+        anchor = (E + 127) << 7 if E >= -126 else 1 << (E + 133)
+        if e_s == -127:
+            anchor = (-119 + 127) << 7                   # any amax with E <= -119
+        limit = (E + 128) << 7 if E + 128 <= 0xFF else 0x7F80
+        cand = mags[mags < limit]
+        xs = np.concatenate([cand, cand | 0x8000]).astype(np.uint16)
+        pad = (-xs.size) % 31
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        blk = np.empty((xs.shape[0], 32), np.uint16)
+        blk[:, 0] = anchor
+        blk[:, 1:] = xs
+        out.append(blk.ravel())
+    return np.concatenate(out)
+
+
+def test_mxfp8_every_reachable_element_and_scale(zs):
+    import torch
+    x = _reachable_blocks()
+    want_e, want_s = O.mxfp8_pack(x)
+    n = x.size
+    elem = torch.empty(n, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    zs.zero_mxfp8_pack(to_dev(x), elem, scale)
+    torch.cuda.synchronize()
+    ge, gs = from_dev(elem), from_dev(scale)
+    assert np.array_equal(gs, want_s), np.nonzero(gs != want_s)[0][:5]
+    bad = np.nonzero(ge != want_e)[0]
+    assert bad.size == 0, [(hex(int(x[i])), int(want_s[i // 32]) - 127, hex(ge[i]), hex(want_e[i]))
+                           for i in bad[:6]]
 
 
 # ---------------------------------------------------------- determinism --

@@ -33,7 +33,8 @@ class _AdamArgs(C.Structure):
                 ("max_norm", C.c_double), ("check_overflow", C.c_int),
                 ("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
-                ("skipped_out", C.c_void_p)]
+                ("skipped_out", C.c_void_p), ("mx_elem_out", C.c_void_p),
+                ("mx_scale_out", C.c_void_p)]
 
 
 def lib():
@@ -179,7 +180,8 @@ def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:
 def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                     weight_decay=0.0, grad_f32=None, replicas=None, inv_scale=1.0,
                     param_bf16=None, accs=None, max_norm=0.0, check_overflow=False,
-                    skipped_out=None, n=None, stream=None) -> None:
+                    skipped_out=None, mx_elem_out=None, mx_scale_out=None, n=None,
+                    stream=None) -> None:
     n = master.numel() if n is None else int(n)
     for name, t in (("m", m), ("v", v)):
         if t.numel() < n or t.dtype != torch.float32:
@@ -209,6 +211,8 @@ def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                                                       float(eps), float(weight_decay))
     a.step = int(step)
     a.skipped_out = _dev_ptr(skipped_out, "skipped_out")
+    a.mx_elem_out = _dev_ptr(mx_elem_out, "mx_elem_out")
+    a.mx_scale_out = _dev_ptr(mx_scale_out, "mx_scale_out")
     rc = lib().zero_adamw_step(C.byref(a), _stream(stream))
     del keep
     _check(rc, "zero_adamw_step")

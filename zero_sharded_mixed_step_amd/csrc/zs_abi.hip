@@ -141,8 +141,12 @@ int zero_adamw_step(const zero_adamw_args* a, void* stream) {
     if (!aligned16(a->master) || !aligned16(a->m) || !aligned16(a->v) ||
         (a->grad_f32 && !aligned16(a->grad_f32)) ||
         (a->param_bf16 && !aligned16(a->param_bf16)) || (a->accs && !aligned16(a->accs)) ||
-        (a->skipped_out && !aligned4(a->skipped_out)))
+        (a->skipped_out && !aligned4(a->skipped_out)) ||
+        (a->mx_elem_out && !aligned16(a->mx_elem_out)) ||
+        (a->mx_scale_out && !aligned16(a->mx_scale_out)))
       return ZERO_EALIGN;
+    if ((a->mx_elem_out == nullptr) != (a->mx_scale_out == nullptr)) return ZERO_EINVAL;
+    if (a->mx_elem_out != nullptr && a->n % 32 != 0) return ZERO_ESIZE;
     zs::AdamLaunch L;
     L.grad = a->grad_f32;
     L.replicas = a->replicas;
@@ -153,6 +157,8 @@ int zero_adamw_step(const zero_adamw_args* a, void* stream) {
     L.m = a->m;
     L.v = a->v;
     L.param = a->param_bf16;
+    L.mx_elem = a->mx_elem_out;
+    L.mx_scale = a->mx_scale_out;
     L.accs = a->n_accs > 0 ? a->accs : nullptr;
     L.n_accs = a->n_accs;
     L.max_norm = a->max_norm;

@@ -25,6 +25,26 @@ struct Replicas {
 
 // ------------------------------------------------------------- loads ------
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming-access policy per access: nontemporal (NT) loads/stores tell the
+// memory system not to keep the lines, which suits data touched exactly once
+// (gradient replicas, the averaged gradient).  The in-place AdamW state is
+// read and rewritten through the cache (measured faster on MI355X).
+template <bool NT, typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
@@ -32,14 +52,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
 // Eight elements of one replica as fp32 (bf16 widening is exact).  `full`
 // is false only for the final, partial chunk: its elements past `n` read as
 // +0 and nothing beyond the buffer is touched.
-template <int DT>
+template <int DT, bool NT>
 __device__ __forceinline__ void load_chunk(const void* base, uint64_t c, bool full,
                                            uint64_t n, float x[kVec]) {
   const uint64_t e0 = c * kVec;
-  if (DT == ZERO_BF16) {
+  if constexpr (DT == ZERO_BF16) {
     const uint16_t* p = static_cast<const uint16_t*>(base) + e0;
     if (full) {
-      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      const u32x4 w = load_stream<NT>(reinterpret_cast<const u32x4*>(p));
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -53,8 +73,8 @@ __device__ __forceinline__ void load_chunk(const void* base, uint64_t c, bool fu
   } else {
     const float* p = static_cast<const float*>(base) + e0;
     if (full) {
-      const float4 a = *reinterpret_cast<const float4*>(p);
-      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      const f32x4 a = load_stream<NT>(reinterpret_cast<const f32x4*>(p));
+      const f32x4 b = load_stream<NT>(reinterpret_cast<const f32x4*>(p + 4));
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
       x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     } else {
@@ -64,17 +84,19 @@ __device__ __forceinline__ void load_chunk(const void* base, uint64_t c, bool fu
   }
 }
 
+template <bool NT>
 __device__ __forceinline__ void load_f32_chunk(const float* base, uint64_t c, bool full,
                                                uint64_t n, float x[kVec]) {
-  load_chunk<ZERO_F32>(base, c, full, n, x);
+  load_chunk<ZERO_F32, NT>(base, c, full, n, x);
 }
 
+template <bool NT>
 __device__ __forceinline__ void store_f32_chunk(float* base, uint64_t c, bool full,
                                                 uint64_t n, const float x[kVec]) {
   float* p = base + c * kVec;
   if (full) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    store_stream<NT>(reinterpret_cast<f32x4*>(p), f32x4{x[0], x[1], x[2], x[3]});
+    store_stream<NT>(reinterpret_cast<f32x4*>(p + 4), f32x4{x[4], x[5], x[6], x[7]});
   } else {
     const uint64_t e0 = c * kVec;
 #pragma unroll
@@ -87,14 +109,14 @@ __device__ __forceinline__ void store_f32_chunk(float* base, uint64_t c, bool fu
 
 // g = (r_0 + r_1 + ... + r_{P-1}) * inv_scale in binary32, rank order.
 // PT > 0 fixes P at compile time (all P loads issue before the adds);
-// PT == 0 reads the runtime count.
+// PT == 0 reads the runtime count.  Replicas are read once: NT loads.
 template <int DT, int PT>
 __device__ __forceinline__ void reduce_chunk(const Replicas& R, int P, uint64_t c, bool full,
                                              uint64_t n, float inv_scale, float g[kVec]) {
   if constexpr (PT > 0) {
     float x[PT][kVec];
 #pragma unroll
-    for (int k = 0; k < PT; ++k) load_chunk<DT>(R.p[k], c, full, n, x[k]);
+    for (int k = 0; k < PT; ++k) load_chunk<DT, true>(R.p[k], c, full, n, x[k]);
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       float s = x[0][j];
@@ -104,15 +126,72 @@ __device__ __forceinline__ void reduce_chunk(const Replicas& R, int P, uint64_t 
     }
   } else {
     float s[kVec];
-    load_chunk<DT>(R.p[0], c, full, n, s);
+    load_chunk<DT, true>(R.p[0], c, full, n, s);
     for (int k = 1; k < P; ++k) {
       float x[kVec];
-      load_chunk<DT>(R.p[k], c, full, n, x);
+      load_chunk<DT, true>(R.p[k], c, full, n, x);
 #pragma unroll
       for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[j];
     }
 #pragma unroll
     for (int j = 0; j < kVec; ++j) g[j] = s[j] * inv_scale;
+  }
+}
+
+// Two-phase form of reduce_chunk for whole chunks (PT > 0): `Raw` holds the
+// undecoded 16-byte vectors of all replicas, so a caller can issue the loads
+// of several chunks before any of them is summed.
+template <int DT, int PT>
+struct RawChunk {
+  static constexpr int kWords = DT == ZERO_BF16 ? 1 : 2;  // 16-byte vectors per replica
+  u32x4 w[PT][kWords];
+};
+
+template <int DT, int PT>
+__device__ __forceinline__ void load_raw(const Replicas& R, uint64_t c, RawChunk<DT, PT>& r) {
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    if constexpr (DT == ZERO_BF16) {
+      r.w[k][0] = load_stream<true>(
+          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(R.p[k]) + c * kVec));
+    } else {
+      const u32x4* p =
+          reinterpret_cast<const u32x4*>(static_cast<const float*>(R.p[k]) + c * kVec);
+      r.w[k][0] = load_stream<true>(p);
+      r.w[k][1] = load_stream<true>(p + 1);
+    }
+  }
+}
+
+template <int DT, int PT>
+__device__ __forceinline__ void sum_raw(const RawChunk<DT, PT>& r, float inv_scale,
+                                        float g[kVec]) {
+  float x[PT][kVec];
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    if constexpr (DT == ZERO_BF16) {
+      const uint32_t ws[4] = {r.w[k][0].x, r.w[k][0].y, r.w[k][0].z, r.w[k][0].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[k][2 * j] = __uint_as_float(ws[j] << 16);
+        x[k][2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        x[k][4 * h + 0] = __uint_as_float(r.w[k][h].x);
+        x[k][4 * h + 1] = __uint_as_float(r.w[k][h].y);
+        x[k][4 * h + 2] = __uint_as_float(r.w[k][h].z);
+        x[k][4 * h + 3] = __uint_as_float(r.w[k][h].w);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    float s = x[0][j];
+#pragma unroll
+    for (int k = 1; k < PT; ++k) s = s + x[k][j];
+    g[j] = s * inv_scale;
   }
 }
 
@@ -189,6 +268,98 @@ __device__ __forceinline__ void fixed_point_piece(double S, int quad_lane, int& 
   const uint32_t mine = quad_lane == 0 ? p0 : (quad_lane == 1 ? p1 : (quad_lane == 2 ? p2 : 0u));
   piece = mine;
   digit = base + (quad_lane < 3 ? quad_lane : 0);
+}
+
+// -------------------------------------------------------------- MXFP8 ----
+
+
+__device__ __forceinline__ int dpp_quad_int(int x, int which) {
+  return which == 1 ? __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false)
+                    : __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+}
+
+// One 32-element block held by a quad of lanes (8 bf16 per lane): block
+// scale byte (returned, same in all four lanes) and this lane's 8 codes.
+// Must be reached by all 64 lanes.
+__device__ __forceinline__ uint32_t mx_quad_encode(const uint32_t xs[kVec], uint32_t codes[kVec]) {
+  int special = 0;
+  int amax = 0;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const int mag = static_cast<int>(xs[j] & 0x7FFFu);
+    special |= (mag >= 0x7F80) ? 1 : 0;
+    amax = mag > amax ? mag : amax;
+  }
+  special |= dpp_quad_int(special, 1);
+  special |= dpp_quad_int(special, 2);
+  {
+    const int o1 = dpp_quad_int(amax, 1);
+    amax = o1 > amax ? o1 : amax;
+    const int o2 = dpp_quad_int(amax, 2);
+    amax = o2 > amax ? o2 : amax;
+  }
+  uint32_t sbyte;
+  if (special) {
+    sbyte = 0xFFu;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) codes[j] = ((xs[j] >> 8) & 0x80u) | 0x7Fu;
+  } else if (amax == 0) {
+    sbyte = 0x00u;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) codes[j] = (xs[j] >> 8) & 0x80u;
+  } else {
+    const int ex = amax >> 7;
+    const int E = ex ? ex - 127 : -133 + (31 - __clz(amax & 0x7F));
+    int e_s = E - 8;
+    e_s = e_s < -127 ? -127 : (e_s > 127 ? 127 : e_s);
+    sbyte = static_cast<uint32_t>(e_s + 127);
+    // Element codes: q = x * 2^-e_s is exact in binary32 whenever it can
+    // matter (|q| >= 2^-126; anything smaller encodes to a signed zero either
+    // way); clamping to +-448 gives the saturation; v_cvt_pk_fp8_f32 then
+    // rounds to nearest even onto the E4M3FN grid (subnormal step 2^-9).
+    // Checked bit for bit against the CPU oracle for every bf16 value under
+    // every scale exponent a block can produce.
+    const float scale = __uint_as_float(static_cast<uint32_t>(127 - e_s) << 23);
+#pragma unroll
+    for (int j = 0; j < kVec; j += 2) {
+      float q0 = __uint_as_float(xs[j] << 16) * scale;
+      float q1 = __uint_as_float(xs[j + 1] << 16) * scale;
+      q0 = __builtin_fminf(__builtin_fmaxf(q0, -448.0f), 448.0f);
+      q1 = __builtin_fminf(__builtin_fmaxf(q1, -448.0f), 448.0f);
+      const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false));
+      codes[j] = pk & 0xFFu;
+      codes[j + 1] = (pk >> 8) & 0xFFu;
+    }
+  }
+  return sbyte;
+}
+
+// Stores of one chunk's codes (8 bytes) and, from lane 16i, the scale bytes
+// of the four quads 16i, 16i+4, 16i+8, 16i+12 (consecutive blocks).  All 64
+// lanes must call it (the scale gather is a cross-lane read); `valid` masks
+// the stores of lanes past the end.  nchunks is a multiple of 4.
+__device__ __forceinline__ void mx_store(uint8_t* elem, uint8_t* scale, uint64_t c,
+                                         uint64_t nchunks, bool valid,
+                                         const uint32_t codes[kVec], uint32_t sbyte) {
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  if (valid) {
+    const u32x2 out = {codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24),
+                       codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24)};
+    store_stream<false>(reinterpret_cast<u32x2*>(elem + c * kVec), out);
+  }
+  const uint32_t s1 = __shfl(sbyte, lane + 4);
+  const uint32_t s2 = __shfl(sbyte, lane + 8);
+  const uint32_t s3 = __shfl(sbyte, lane + 12);
+  if ((lane & 15) == 0 && valid) {
+    const uint64_t b = c / 4;  // block index, a multiple of 4
+    const uint64_t nblocks = nchunks / 4;
+    if (b + 4 <= nblocks) {
+      *reinterpret_cast<uint32_t*>(scale + b) = sbyte | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    } else {
+      const uint32_t sv[4] = {sbyte, s1, s2, s3};
+      for (uint64_t k = 0; b + k < nblocks; ++k) scale[b + k] = static_cast<uint8_t>(sv[k]);
+    }
+  }
 }
 
 // ----------------------------------------------------------- the gate ----

@@ -14,9 +14,17 @@ struct AdamScalars {
   float b1, b2, omb1, omb2, step_size, sqrt_bc2, decay, eps;
 };
 
-// Workgroups per compute unit of the persistent grids (a build-time knob).
-#ifndef ZS_BLOCKS_PER_CU
-#define ZS_BLOCKS_PER_CU 4
+// Workgroups (of 256 threads) per compute unit of each persistent grid,
+// from a sweep of 1..8 on MI355X: the reduce pass needs 4 to keep enough
+// loads in flight, AdamW and the pack run best at 8.
+#ifndef ZS_REDUCE_BLOCKS_PER_CU
+#define ZS_REDUCE_BLOCKS_PER_CU 4
+#endif
+#ifndef ZS_ADAMW_BLOCKS_PER_CU
+#define ZS_ADAMW_BLOCKS_PER_CU 8
+#endif
+#ifndef ZS_PACK_BLOCKS_PER_CU
+#define ZS_PACK_BLOCKS_PER_CU 8
 #endif
 
 int compute_units(int device);
@@ -35,6 +43,8 @@ struct AdamLaunch {
   float* m;
   float* v;
   uint16_t* param;
+  uint8_t* mx_elem;
+  uint8_t* mx_scale;
   const zero_norm_acc* accs;
   int n_accs;
   double max_norm;

@@ -26,11 +26,11 @@ int compute_units(int device) {
   return cus;
 }
 
-static unsigned grid_for(uint64_t nchunks) {
+static unsigned grid_for(uint64_t nchunks, int blocks_per_cu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   const uint64_t ntiles = (nchunks + kThreads - 1) / kThreads;
-  const uint64_t cap = static_cast<uint64_t>(compute_units(dev)) * ZS_BLOCKS_PER_CU;
+  const uint64_t cap = static_cast<uint64_t>(compute_units(dev)) * blocks_per_cu;
   const uint64_t g = ntiles < cap ? ntiles : cap;
   return static_cast<unsigned>(g > 0 ? g : 1);
 }
@@ -53,6 +53,10 @@ struct ReduceParams {
   zero_norm_acc* acc;
 };
 
+#ifndef ZS_REDUCE_LOADS
+#define ZS_REDUCE_LOADS 32
+#endif
+
 template <int DT, int PT, bool WRITE, bool NORM>
 __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm) {
   __shared__ uint64_t s_digit[NORM ? 7 : 1][kThreads];
@@ -64,27 +68,66 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
     for (int k = 0; k < 7; ++k) s_digit[k][tid] = 0;
   }
   uint32_t nonfinite = 0, overflow = 0;
+  // Norm state of one chunk; reached by all 64 lanes (quad DPP inside).
+  auto norm_chunk = [&](const float g[kVec]) {
+    const double a = chunk_sumsq(g, nonfinite);
+    const double S = quad_group_sum(a);
+    if (quad_lane == 0 && S >= 18446744073709551616.0) ++overflow;
+    int d;
+    uint64_t piece;
+    fixed_point_piece(S, quad_lane, d, piece);
+    if (piece != 0) s_digit[d][tid] += piece;  // lane-private row
+  };
+  // Chunks per lane per fast-path iteration: enough to keep about 16
+  // 16-byte loads in flight per lane whatever P and the dtype are.
+  constexpr int kRawLoads = PT > 0 ? PT * (DT == ZERO_BF16 ? 1 : 2) : 8;
+  constexpr int U = ZS_REDUCE_LOADS / kRawLoads < 1 ? 1
+                    : (ZS_REDUCE_LOADS / kRawLoads > 8 ? 8 : ZS_REDUCE_LOADS / kRawLoads);
   const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
-  for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint64_t c = tile * kThreads + tid;
-    const bool valid = c < prm.nchunks;
-    const bool full = valid && (c * kVec + kVec <= prm.n);
-    float g[kVec];
-    if (valid) {
-      reduce_chunk<DT, PT>(prm.R, prm.P, c, full, prm.n, prm.inv_scale, g);
-      if (WRITE) store_f32_chunk(prm.g_out, c, full, prm.n, g);
+  const uint64_t full_tiles = prm.n / (static_cast<uint64_t>(kThreads) * kVec);
+  const uint64_t step = static_cast<uint64_t>(gridDim.x) * U;
+  uint64_t tile = static_cast<uint64_t>(blockIdx.x) * U;
+  // Fast path: U whole tiles, no bounds checks, all loads issued up front.
+  for (; tile + U <= full_tiles; tile += step) {
+    if constexpr (PT > 0) {
+      RawChunk<DT, PT> raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_raw<DT, PT>(prm.R, (tile + u) * kThreads + tid, raw[u]);
+      __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first wait
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float g[kVec];
+        sum_raw<DT, PT>(raw[u], prm.inv_scale, g);
+        if (WRITE) store_f32_chunk<true>(prm.g_out, (tile + u) * kThreads + tid, true, prm.n, g);
+        if constexpr (NORM) norm_chunk(g);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) g[j] = 0.0f;
+      for (int u = 0; u < U; ++u) {
+        float g[kVec];
+        reduce_chunk<DT, PT>(prm.R, prm.P, (tile + u) * kThreads + tid, true, prm.n,
+                             prm.inv_scale, g);
+        if (WRITE) store_f32_chunk<true>(prm.g_out, (tile + u) * kThreads + tid, true, prm.n, g);
+        if constexpr (NORM) norm_chunk(g);
+      }
     }
-    if constexpr (NORM) {
-      const double a = chunk_sumsq(g, nonfinite);
-      const double S = quad_group_sum(a);  // all 64 lanes take part
-      if (quad_lane == 0 && S >= 18446744073709551616.0) ++overflow;
-      int d;
-      uint64_t piece;
-      fixed_point_piece(S, quad_lane, d, piece);
-      if (piece != 0) s_digit[d][tid] += piece;  // lane-private row
+  }
+  // Tail: the remaining tiles of this workgroup one by one, with checks.
+  for (; tile < ntiles; tile += step) {
+    for (int u = 0; u < U; ++u) {
+      if (tile + u >= ntiles) break;  // uniform across the workgroup
+      const uint64_t c = (tile + u) * kThreads + tid;
+      const bool valid = c < prm.nchunks;
+      const bool full = valid && (c * kVec + kVec <= prm.n);
+      float g[kVec];
+      if (valid) {
+        reduce_chunk<DT, PT>(prm.R, prm.P, c, full, prm.n, prm.inv_scale, g);
+        if (WRITE) store_f32_chunk<true>(prm.g_out, c, full, prm.n, g);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) g[j] = 0.0f;
+      }
+      if constexpr (NORM) norm_chunk(g);
     }
   }
   if constexpr (NORM) {
@@ -151,7 +194,7 @@ hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t
   prm.nchunks = (n + kVec - 1) / kVec;
   prm.g_out = g_out;
   prm.acc = acc;
-  const unsigned grid = grid_for(prm.nchunks);
+  const unsigned grid = grid_for(prm.nchunks, ZS_REDUCE_BLOCKS_PER_CU);
   if (dtype == ZERO_BF16)
     reduce_dispatch_p<ZERO_BF16>(prm, g_out != nullptr, acc != nullptr, grid, stream);
   else
@@ -176,6 +219,8 @@ struct AdamParams {
   float* m;
   float* v;
   uint16_t* param;
+  uint8_t* mx_elem;
+  uint8_t* mx_scale;
   const zero_norm_acc* accs;
   int n_accs;
   int check_overflow;
@@ -186,8 +231,14 @@ struct AdamParams {
   AdamScalars s;
 };
 
+#ifndef ZS_ADAMW_UNROLL
+#define ZS_ADAMW_UNROLL 2
+#endif
+
 // SRC < 0: gradient from prm.grad (fp32); otherwise the replica dtype.
-template <int SRC, int PT, bool PARAM>
+// MX: also pack the new bf16 params to MXFP8 (n % 32 == 0); the loop then
+// stays wave-uniform because the block amax is a quad DPP reduction.
+template <int SRC, int PT, bool PARAM, bool MX>
 __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
   __shared__ Gate s_gate;
   if (threadIdx.x == 0) {
@@ -201,20 +252,10 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
   const float coef = gt.coef;
   const AdamScalars sc = prm.s;
   const float neg_step = -sc.step_size;
-  const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
-  for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint64_t c = tile * kThreads + threadIdx.x;
-    if (c >= prm.nchunks) break;
-    const bool full = c * kVec + kVec <= prm.n;
-    float g[kVec], th[kVec], mm[kVec], vv[kVec];
-    if constexpr (SRC < 0)
-      load_f32_chunk(prm.grad, c, full, prm.n, g);
-    else
-      reduce_chunk<SRC, PT>(prm.R, prm.P, c, full, prm.n, prm.inv_scale, g);
-    load_f32_chunk(prm.master, c, full, prm.n, th);
-    load_f32_chunk(prm.m, c, full, prm.n, mm);
-    load_f32_chunk(prm.v, c, full, prm.n, vv);
-    uint32_t pb[kVec];
+  // The update of one chunk from its loaded g and state; stores the new
+  // state and param and leaves the param bits in pb (for the MXFP8 epilogue).
+  auto update_chunk = [&](uint64_t c, bool full, const float g[kVec], float th[kVec],
+                          float mm[kVec], float vv[kVec], uint32_t pb[kVec]) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       const float gc = g[j] * coef;
@@ -228,19 +269,81 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
       vv[j] = vi;
       pb[j] = bf16_rne_bits(t);
     }
-    store_f32_chunk(prm.master, c, full, prm.n, th);
-    store_f32_chunk(prm.m, c, full, prm.n, mm);
-    store_f32_chunk(prm.v, c, full, prm.n, vv);
+    store_f32_chunk<false>(prm.master, c, full, prm.n, th);
+    store_f32_chunk<false>(prm.m, c, full, prm.n, mm);
+    store_f32_chunk<false>(prm.v, c, full, prm.n, vv);
     if (PARAM) {
       uint16_t* p = prm.param + c * kVec;
       if (full) {
-        *reinterpret_cast<uint4*>(p) =
-            make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                       pb[6] | (pb[7] << 16));
+        store_stream<false>(reinterpret_cast<u32x4*>(p),
+                            u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
+                                  pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16)});
       } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j)
           if (c * kVec + j < prm.n) p[j] = static_cast<uint16_t>(pb[j]);
+      }
+    }
+  };
+  constexpr int U = ZS_ADAMW_UNROLL;
+  const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
+  const uint64_t full_tiles = prm.n / (static_cast<uint64_t>(kThreads) * kVec);
+  const uint64_t step = static_cast<uint64_t>(gridDim.x) * U;
+  uint64_t tile = static_cast<uint64_t>(blockIdx.x) * U;
+  // Fast path: U whole tiles, no bounds checks, every load issued first.
+  for (; tile + U <= full_tiles; tile += step) {
+    float g[U][kVec], th[U][kVec], mm[U][kVec], vv[U][kVec];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t c = (tile + u) * kThreads + threadIdx.x;
+      if constexpr (SRC < 0)
+        load_f32_chunk<false>(prm.grad, c, true, prm.n, g[u]);
+      else
+        reduce_chunk<SRC, PT>(prm.R, prm.P, c, true, prm.n, prm.inv_scale, g[u]);
+      load_f32_chunk<false>(prm.master, c, true, prm.n, th[u]);
+      load_f32_chunk<false>(prm.m, c, true, prm.n, mm[u]);
+      load_f32_chunk<false>(prm.v, c, true, prm.n, vv[u]);
+    }
+    if constexpr (U > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t c = (tile + u) * kThreads + threadIdx.x;
+      uint32_t pb[kVec];
+      update_chunk(c, true, g[u], th[u], mm[u], vv[u], pb);
+      if constexpr (MX) {
+        uint32_t codes[kVec];
+        const uint32_t sbyte = mx_quad_encode(pb, codes);
+        mx_store(prm.mx_elem, prm.mx_scale, c, prm.nchunks, true, codes, sbyte);
+      }
+    }
+  }
+  // Tail: remaining tiles one by one with bounds checks (wave-uniform loop,
+  // as the MXFP8 epilogue needs all lanes).
+  for (; tile < ntiles; tile += step) {
+    for (int u = 0; u < U; ++u) {
+      if (tile + u >= ntiles) break;
+      const uint64_t c = (tile + u) * kThreads + threadIdx.x;
+      const bool valid = c < prm.nchunks;
+      uint32_t pb[kVec];
+      if (valid) {
+        const bool full = c * kVec + kVec <= prm.n;
+        float g[kVec], th[kVec], mm[kVec], vv[kVec];
+        if constexpr (SRC < 0)
+          load_f32_chunk<false>(prm.grad, c, full, prm.n, g);
+        else
+          reduce_chunk<SRC, PT>(prm.R, prm.P, c, full, prm.n, prm.inv_scale, g);
+        load_f32_chunk<false>(prm.master, c, full, prm.n, th);
+        load_f32_chunk<false>(prm.m, c, full, prm.n, mm);
+        load_f32_chunk<false>(prm.v, c, full, prm.n, vv);
+        update_chunk(c, full, g, th, mm, vv, pb);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) pb[j] = 0u;
+      }
+      if constexpr (MX) {
+        uint32_t codes[kVec];
+        const uint32_t sbyte = mx_quad_encode(pb, codes);
+        mx_store(prm.mx_elem, prm.mx_scale, c, prm.nchunks, valid, codes, sbyte);
       }
     }
   }
@@ -248,10 +351,15 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
 
 template <int SRC, int PT>
 static void adamw_dispatch_param(const AdamParams& prm, unsigned grid, hipStream_t st) {
-  if (prm.param != nullptr)
-    hipLaunchKernelGGL((adamw_kernel<SRC, PT, true>), dim3(grid), dim3(kThreads), 0, st, prm);
+  const bool param = prm.param != nullptr, mx = prm.mx_elem != nullptr;
+  if (mx && param)
+    hipLaunchKernelGGL((adamw_kernel<SRC, PT, true, true>), dim3(grid), dim3(kThreads), 0, st, prm);
+  else if (mx)
+    hipLaunchKernelGGL((adamw_kernel<SRC, PT, false, true>), dim3(grid), dim3(kThreads), 0, st, prm);
+  else if (param)
+    hipLaunchKernelGGL((adamw_kernel<SRC, PT, true, false>), dim3(grid), dim3(kThreads), 0, st, prm);
   else
-    hipLaunchKernelGGL((adamw_kernel<SRC, PT, false>), dim3(grid), dim3(kThreads), 0, st, prm);
+    hipLaunchKernelGGL((adamw_kernel<SRC, PT, false, false>), dim3(grid), dim3(kThreads), 0, st, prm);
 }
 
 template <int DT>
@@ -275,6 +383,8 @@ hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream) {
   prm.m = a.m;
   prm.v = a.v;
   prm.param = a.param;
+  prm.mx_elem = a.mx_elem;
+  prm.mx_scale = a.mx_scale;
   prm.accs = a.accs;
   prm.n_accs = a.n_accs;
   prm.check_overflow = a.check_overflow;
@@ -283,7 +393,7 @@ hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream) {
   prm.n = a.n;
   prm.nchunks = (a.n + kVec - 1) / kVec;
   prm.s = a.s;
-  const unsigned grid = grid_for(prm.nchunks);
+  const unsigned grid = grid_for(prm.nchunks, ZS_ADAMW_BLOCKS_PER_CU);
   if (a.grad != nullptr)
     adamw_dispatch_param<-1, 1>(prm, grid, stream);
   else if (a.dtype == ZERO_BF16)
@@ -327,113 +437,39 @@ hipError_t launch_acc_clear(zero_norm_acc* accs, int n_accs, hipStream_t stream)
 
 // -------------------------------------------------------------- MXFP8 ----
 
-__device__ __forceinline__ int dpp_quad_int(int x, int which) {
-  return which == 1 ? __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false)
-                    : __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
-}
+#ifndef ZS_MX_UNROLL
+#define ZS_MX_UNROLL 4
+#endif
 
-// E4M3FN code of bf16 x scaled by 2^-e_s: round to nearest even on the E4M3
-// grid (bias 7, subnormal step 2^-9), saturating at 448, sign kept.  Pure
-// integer arithmetic on the bf16 bits.
-__device__ __forceinline__ uint32_t e4m3_code(uint32_t x, int e_s) {
-  const uint32_t sign = (x >> 8) & 0x80u;
-  const uint32_t mag = x & 0x7FFFu;
-  if (mag == 0) return sign;
-  const int ex = static_cast<int>(mag >> 7);
-  const uint32_t M = ex ? ((mag & 0x7Fu) | 0x80u) : (mag & 0x7Fu);
-  const int base = (ex ? ex : 1) - 134 - e_s;  // value = M * 2^base
-  const int msb = 31 - __clz(static_cast<int>(M));
-  const int Eq = base + msb;                   // floor(log2 |q|)
-  const int qe = (Eq > -6 ? Eq : -6) - 3;      // exponent of the E4M3 step
-  const int sh = qe - base;                    // >= -3
-  uint32_t k;
-  if (sh <= 0) {
-    k = M << (-sh);
-  } else {
-    const int s = sh > 31 ? 31 : sh;
-    k = M >> s;
-    const uint32_t rem = M & ((1u << s) - 1u);
-    const uint32_t half = 1u << (s - 1);
-    if (rem > half || (rem == half && (k & 1u))) ++k;
-  }
-  uint32_t code = (static_cast<uint32_t>(qe + 9) << 3) + k;
-  if (code > 0x7Eu) code = 0x7Eu;
-  return sign | code;
-}
-
+// ZS_MX_UNROLL tiles per iteration, so that several 16-byte loads per lane
+// are in flight before the integer encoding starts.
 __global__ void __launch_bounds__(kThreads) mxfp8_kernel(const uint16_t* in, uint64_t nchunks,
                                                          uint8_t* elem, uint8_t* scale) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const uint64_t ntiles = (nchunks + kThreads - 1) / kThreads;
-  for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint64_t c = tile * kThreads + tid;
-    const bool valid = c < nchunks;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (valid) {
-      const uint4 v = *reinterpret_cast<const uint4*>(in + c * kVec);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    }
-    uint32_t xs[kVec];
+  constexpr int U = ZS_MX_UNROLL;
+  for (uint64_t tile = static_cast<uint64_t>(blockIdx.x) * U; tile < ntiles;
+       tile += static_cast<uint64_t>(gridDim.x) * U) {
+    uint32_t xs[U][kVec];
+    bool valid[U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xs[2 * j] = w[j] & 0xFFFFu;
-      xs[2 * j + 1] = w[j] >> 16;
-    }
-    int special = 0;
-    int amax = 0;
+    for (int u = 0; u < U; ++u) {
+      const uint64_t c = (tile + u) * kThreads + threadIdx.x;
+      valid[u] = (tile + u) < ntiles && c < nchunks;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (valid[u]) w = load_stream<false>(reinterpret_cast<const u32x4*>(in + c * kVec));
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const int mag = static_cast<int>(xs[j] & 0x7FFFu);
-      special |= (mag >= 0x7F80) ? 1 : 0;
-      amax = mag > amax ? mag : amax;
-    }
-    special |= dpp_quad_int(special, 1);
-    special |= dpp_quad_int(special, 2);
-    {
-      const int o1 = dpp_quad_int(amax, 1);
-      amax = o1 > amax ? o1 : amax;
-      const int o2 = dpp_quad_int(amax, 2);
-      amax = o2 > amax ? o2 : amax;
-    }
-    uint32_t sbyte;
-    uint32_t codes[kVec];
-    if (special) {
-      sbyte = 0xFFu;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) codes[j] = ((xs[j] >> 8) & 0x80u) | 0x7Fu;
-    } else if (amax == 0) {
-      sbyte = 0x00u;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) codes[j] = (xs[j] >> 8) & 0x80u;
-    } else {
-      const int ex = amax >> 7;
-      const int E = ex ? ex - 127 : -133 + (31 - __clz(amax & 0x7F));
-      int e_s = E - 8;
-      e_s = e_s < -127 ? -127 : (e_s > 127 ? 127 : e_s);
-      sbyte = static_cast<uint32_t>(e_s + 127);
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) codes[j] = e4m3_code(xs[j], e_s);
-    }
-    if (valid) {
-      uint2 out;
-      out.x = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
-      out.y = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
-      *reinterpret_cast<uint2*>(elem + c * kVec) = out;
-    }
-    // scale bytes: lane 16i gathers the four quads 16i, 16i+4, 16i+8, 16i+12
-    const uint32_t s1 = __shfl(sbyte, lane + 4);
-    const uint32_t s2 = __shfl(sbyte, lane + 8);
-    const uint32_t s3 = __shfl(sbyte, lane + 12);
-    if ((lane & 15) == 0 && valid) {
-      const uint64_t b = c / 4;  // block index, a multiple of 4
-      const uint64_t nblocks = nchunks / 4;
-      if (b + 4 <= nblocks) {
-        *reinterpret_cast<uint32_t*>(scale + b) = sbyte | (s1 << 8) | (s2 << 16) | (s3 << 24);
-      } else {
-        const uint32_t sv[4] = {sbyte, s1, s2, s3};
-        for (uint64_t k = 0; b + k < nblocks; ++k) scale[b + k] = static_cast<uint8_t>(sv[k]);
+      for (int j = 0; j < 4; ++j) {
+        xs[u][2 * j] = ws[j] & 0xFFFFu;
+        xs[u][2 * j + 1] = ws[j] >> 16;
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t c = (tile + u) * kThreads + threadIdx.x;
+      uint32_t codes[kVec];
+      const uint32_t sbyte = mx_quad_encode(xs[u], codes);
+      mx_store(elem, scale, c, nchunks, valid[u], codes, sbyte);
     }
   }
 }
@@ -441,7 +477,7 @@ __global__ void __launch_bounds__(kThreads) mxfp8_kernel(const uint16_t* in, uin
 hipError_t launch_mxfp8(const uint16_t* in, uint64_t n, uint8_t* elem, uint8_t* scale,
                         hipStream_t stream) {
   const uint64_t nchunks = n / kVec;
-  const unsigned grid = grid_for(nchunks);
+  const unsigned grid = grid_for(nchunks, ZS_PACK_BLOCKS_PER_CU);
   hipLaunchKernelGGL(mxfp8_kernel, dim3(grid), dim3(kThreads), 0, stream, in, nchunks, elem,
                      scale);
   return hipGetLastError();

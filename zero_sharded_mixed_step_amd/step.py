@@ -17,6 +17,10 @@ The reduce runs bucket by bucket when `bucket` is set; the norm state of all
 buckets accumulates in one accumulator (integer sums, so bucketing changes no
 bit of the result).
 
+MXFP8: with `pack`, the AdamW pass also writes the MXFP8 pack of the new
+bf16 params (codes + block scales), saving the re-read of the bf16 param
+shard and a launch; `pack_param()` runs the standalone pack kernel.
+
 Step counter: `t` counts applied updates.  With the overflow check on, the
 device decides the skip; the flag travels to pinned host memory behind an
 event and is read just before the next step's AdamW launch, after that
@@ -35,7 +39,7 @@ class ShardStep:
                  weight_decay: float = 0.0, max_norm: float = 0.0,
                  check_overflow: bool = False, loss_scale: float = 1.0,
                  bucket: Optional[int] = None, pack: bool = False,
-                 path: Optional[str] = None, device="cuda"):
+                 fuse_pack: bool = True, path: Optional[str] = None, device="cuda"):
         self.n, self.P = int(n), int(P)
         self.lr, self.beta1, self.beta2, self.eps, self.wd = lr, beta1, beta2, eps, weight_decay
         self.max_norm, self.check_overflow = float(max_norm), bool(check_overflow)
@@ -67,6 +71,7 @@ class ShardStep:
         self._skip_event = None
         self.t = 0
         self.pack = pack
+        self.fuse_pack = bool(pack and fuse_pack)
         if pack:
             if self.n % 32:
                 raise ValueError("MXFP8 packing needs n % 32 == 0")
@@ -124,6 +129,8 @@ class ShardStep:
             kw["accs"] = self.acc if accs is None else accs
         if self.check_overflow:
             kw["skipped_out"] = self.skipped
+        if self.fuse_pack:
+            kw["mx_elem_out"], kw["mx_scale_out"] = self.mx_elem, self.mx_scale
         if self.path == "materialize":
             B.zero_adamw_step(self.master, self.m, self.v, grad_f32=self.g, **kw)
         else:
@@ -141,10 +148,11 @@ class ShardStep:
 
     def step(self, replicas: List[torch.Tensor], accs: Optional[torch.Tensor] = None) -> None:
         """One whole step: reduce (+ norm), gated AdamW, bf16 param, and the
-        MXFP8 pack of the param shard when enabled."""
+        MXFP8 pack of the param shard when enabled (by default inside the
+        AdamW pass; with fuse_pack=False as a separate pass over the param)."""
         self.reduce(replicas)
         self.update(replicas, accs)
-        if self.pack:
+        if self.pack and not self.fuse_pack:
             self.pack_param()
 
     def applied_steps(self) -> int:
