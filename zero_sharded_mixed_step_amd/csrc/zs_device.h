@@ -278,78 +278,77 @@ __device__ __forceinline__ int dpp_quad_int(int x, int which) {
                     : __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
 }
 
-// One 32-element block held by a quad of lanes (8 bf16 per lane): block
-// scale byte (returned, same in all four lanes) and this lane's 8 codes.
-// Must be reached by all 64 lanes.
-__device__ __forceinline__ uint32_t mx_quad_encode(const uint32_t xs[kVec], uint32_t codes[kVec]) {
-  int special = 0;
-  int amax = 0;
-#pragma unroll
-  for (int j = 0; j < kVec; ++j) {
-    const int mag = static_cast<int>(xs[j] & 0x7FFFu);
-    special |= (mag >= 0x7F80) ? 1 : 0;
-    amax = mag > amax ? mag : amax;
+__device__ __forceinline__ uint32_t dpp_row_shl(uint32_t x, int k) {
+  // lane i of each 16-lane row receives lane i + k of the same row
+  switch (k) {
+    case 4: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x104, 0xF, 0xF, false));
+    case 8: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x108, 0xF, 0xF, false));
+    default: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x10C, 0xF, 0xF, false));
   }
-  special |= dpp_quad_int(special, 1);
-  special |= dpp_quad_int(special, 2);
-  {
-    const int o1 = dpp_quad_int(amax, 1);
-    amax = o1 > amax ? o1 : amax;
-    const int o2 = dpp_quad_int(amax, 2);
-    amax = o2 > amax ? o2 : amax;
+}
+
+// One 32-element block held by a quad of lanes (8 bf16 per lane): returns
+// the block's scale byte (same in all four lanes) and packs this lane's 8
+// codes into words[0..1] (code j in byte j).  Must be reached by all 64
+// lanes.  NaN and inf have the largest bf16 magnitudes, so the integer
+// maximum of the magnitudes also flags a special block.
+__device__ __forceinline__ uint32_t mx_quad_encode(const uint32_t xs[kVec], uint32_t words[2]) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) amax = __builtin_elementwise_max(amax, xs[j] & 0x7FFFu);
+  amax = __builtin_elementwise_max(amax, static_cast<uint32_t>(dpp_quad_int(static_cast<int>(amax), 1)));
+  amax = __builtin_elementwise_max(amax, static_cast<uint32_t>(dpp_quad_int(static_cast<int>(amax), 2)));
+  uint32_t sgn[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    sgn[h] = ((xs[4 * h] >> 8) & 0x80u) | (xs[4 * h + 1] & 0x8000u) |
+             ((xs[4 * h + 2] << 8) & 0x800000u) | ((xs[4 * h + 3] << 16) & 0x80000000u);
+  if (amax >= 0x7F80u) {  // NaN or inf in the block
+    words[0] = sgn[0] | 0x7F7F7F7Fu;
+    words[1] = sgn[1] | 0x7F7F7F7Fu;
+    return 0xFFu;
   }
-  uint32_t sbyte;
-  if (special) {
-    sbyte = 0xFFu;
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) codes[j] = ((xs[j] >> 8) & 0x80u) | 0x7Fu;
-  } else if (amax == 0) {
-    sbyte = 0x00u;
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) codes[j] = (xs[j] >> 8) & 0x80u;
-  } else {
-    const int ex = amax >> 7;
-    const int E = ex ? ex - 127 : -133 + (31 - __clz(amax & 0x7F));
-    int e_s = E - 8;
-    e_s = e_s < -127 ? -127 : (e_s > 127 ? 127 : e_s);
-    sbyte = static_cast<uint32_t>(e_s + 127);
-    // Element codes: q = x * 2^-e_s is exact in binary32 whenever it can
-    // matter (|q| >= 2^-126; anything smaller encodes to a signed zero either
-    // way); clamping to +-448 gives the saturation; v_cvt_pk_fp8_f32 then
-    // rounds to nearest even onto the E4M3FN grid (subnormal step 2^-9).
-    // Checked bit for bit against the CPU oracle for every bf16 value under
-    // every scale exponent a block can produce.
-    const float scale = __uint_as_float(static_cast<uint32_t>(127 - e_s) << 23);
-#pragma unroll
-    for (int j = 0; j < kVec; j += 2) {
-      float q0 = __uint_as_float(xs[j] << 16) * scale;
-      float q1 = __uint_as_float(xs[j + 1] << 16) * scale;
-      q0 = __builtin_fminf(__builtin_fmaxf(q0, -448.0f), 448.0f);
-      q1 = __builtin_fminf(__builtin_fmaxf(q1, -448.0f), 448.0f);
-      const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false));
-      codes[j] = pk & 0xFFu;
-      codes[j + 1] = (pk >> 8) & 0xFFu;
-    }
+  if (amax == 0u) {       // all (signed) zeros
+    words[0] = sgn[0];
+    words[1] = sgn[1];
+    return 0x00u;
   }
-  return sbyte;
+  const int ex = static_cast<int>(amax >> 7);
+  const int E = ex ? ex - 127 : -133 + (31 - __clz(static_cast<int>(amax & 0x7Fu)));
+  const int e_s = E - 8 < -127 ? -127 : E - 8;  // E <= 127, so e_s <= 119
+  // Element codes: q = x * 2^-e_s is exact in binary32 whenever it can
+  // matter (|q| >= 2^-126; anything smaller encodes to a signed zero either
+  // way); the median with +-448 gives the saturation; v_cvt_pk_fp8_f32 then
+  // rounds to nearest even onto the E4M3FN grid (subnormal step 2^-9).
+  // Checked bit for bit against the CPU oracle for every bf16 value under
+  // every scale exponent a block can produce.
+  const float scale = __uint_as_float(static_cast<uint32_t>(127 - e_s) << 23);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      q[j] = __builtin_amdgcn_fmed3f(__uint_as_float(xs[4 * h + j] << 16) * scale, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+    words[h] = static_cast<uint32_t>(w);
+  }
+  return static_cast<uint32_t>(e_s + 127);
 }
 
 // Stores of one chunk's codes (8 bytes) and, from lane 16i, the scale bytes
 // of the four quads 16i, 16i+4, 16i+8, 16i+12 (consecutive blocks).  All 64
-// lanes must call it (the scale gather is a cross-lane read); `valid` masks
-// the stores of lanes past the end.  nchunks is a multiple of 4.
+// lanes must call it (the scale gather reads other lanes); `valid` masks the
+// stores of lanes past the end.  nchunks is a multiple of 4.
 __device__ __forceinline__ void mx_store(uint8_t* elem, uint8_t* scale, uint64_t c,
                                          uint64_t nchunks, bool valid,
-                                         const uint32_t codes[kVec], uint32_t sbyte) {
+                                         const uint32_t words[2], uint32_t sbyte) {
   const int lane = static_cast<int>(threadIdx.x & 63);
-  if (valid) {
-    const u32x2 out = {codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24),
-                       codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24)};
-    store_stream<false>(reinterpret_cast<u32x2*>(elem + c * kVec), out);
-  }
-  const uint32_t s1 = __shfl(sbyte, lane + 4);
-  const uint32_t s2 = __shfl(sbyte, lane + 8);
-  const uint32_t s3 = __shfl(sbyte, lane + 12);
+  if (valid)
+    store_stream<false>(reinterpret_cast<u32x2*>(elem + c * kVec), u32x2{words[0], words[1]});
+  const uint32_t s1 = dpp_row_shl(sbyte, 4);
+  const uint32_t s2 = dpp_row_shl(sbyte, 8);
+  const uint32_t s3 = dpp_row_shl(sbyte, 12);
   if ((lane & 15) == 0 && valid) {
     const uint64_t b = c / 4;  // block index, a multiple of 4
     const uint64_t nblocks = nchunks / 4;
