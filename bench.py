@@ -16,6 +16,7 @@ import argparse
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -23,6 +24,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "include", "zero_step.h")] + [
+    os.path.join(ROOT, "zero_sharded_mixed_step_amd", "csrc", f)
+    for f in ("zs_abi.hip", "zs_device.h", "zs_internal.h", "zs_kernels.hip")]
+# kernel-name fragments of the launch kinds, as rocprofv3 reports them
+KERNEL_NAMES = {"reduce": "shard_reduce_kernel", "adamw": "adamw_kernel",
+                "mxfp8_pack": "mxfp8_kernel"}
+
+
+def source_digest() -> str:
+    """sha256 of the kernel sources: measured traffic is only reported for
+    the exact kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -38,6 +57,11 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM "
                          "byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                          "COPY_WRITE"),
+                    help="no GPU: turn four rocprofv3 --pmc output directories (FETCH_SIZE "
+                         "and WRITE_SIZE of this workload, then of --copy-calibration) "
+                         "into profiles/hbm_traffic.json and a text summary")
     return ap.parse_args()
 
 
@@ -61,6 +85,52 @@ def per_elem_bytes(w, st):
         else:
             kinds["mxfp8_pack"] = 2 + MX_BYTES
     return kinds
+
+
+def _read_counters(d):
+    """{kernel name: [value per dispatch, ...]} from a rocprofv3 csv directory."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(w, dirs, cmdline):
+    """Scale FETCH_SIZE/WRITE_SIZE (KiB per dispatch) by what the same counters
+    read for a plain 1 GiB copy, and store HBM bytes per launch per kind."""
+    fetch, write, cfetch, cwrite = (_read_counters(d) for d in dirs)
+    copy = [k for k in cfetch if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise SystemExit("no copy kernel in the calibration counters")
+    gib = float(1 << 30)
+    f_factor = gib / (1024 * statistics.mean(cfetch[copy[0]]))
+    w_factor = gib / (1024 * statistics.mean(cwrite[copy[0]]))
+    kinds = {}
+    for kind, frag in KERNEL_NAMES.items():
+        fk = [k for k in fetch if frag in k]
+        wk = [k for k in write if frag in k]
+        if not fk or not wk:
+            continue
+        fv = [v for k in fk for v in fetch[k]]
+        wv = [v for k in wk for v in write[k]]
+        kinds[kind] = {"dispatches": len(fv),
+                       "fetch_kib": round(statistics.mean(fv), 1),
+                       "write_kib": round(statistics.mean(wv), 1),
+                       "hbm_bytes": round(1024 * (statistics.mean(fv) * f_factor +
+                                                  statistics.mean(wv) * w_factor))}
+    data = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    data[w.name] = {"source_digest": source_digest(), "fetch_factor": round(f_factor, 4),
+                    "write_factor": round(w_factor, 4), "kinds": kinds, "command": cmdline}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps(data[w.name]))
 
 
 def copy_calibration():
@@ -122,6 +192,11 @@ def main():
         print(f"bench.py measures one GPU only: this build runs each rank's shard step "
               f"on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_pmc:
+        from synth import configs
+        summarize_pmc(configs.ALL[args.config], args.summarize_pmc, " ".join(sys.argv))
+        return
 
     import torch
 
@@ -212,6 +287,14 @@ def main():
                   for k in kinds}
     dom = max(kernel_ms, key=kernel_ms.get)
     dom_gbps = per_kernel[dom]["gbps"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(w.name)
+        if rec and rec["source_digest"] == source_digest() and dom in rec["kinds"]:
+            per_launch = kinds[dom] * w.S if dom != "reduce" or not w.bucket else kinds[dom] * w.bucket
+            traffic = (rec["kinds"][dom]["hbm_bytes"],
+                       round(rec["kinds"][dom]["hbm_bytes"] / per_launch, 4))
     out = {
         "metric": "optimizer-step params/sec per shard + achieved HBM GB/s (% of peak)",
         "value": round(params_per_s, 1),
@@ -238,7 +321,11 @@ def main():
         "standalone_kernels": standalone,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic[0] if traffic else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "scaled by a plain-copy calibration)",
+                     "traffic_vs_algorithmic": traffic[1] if traffic else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

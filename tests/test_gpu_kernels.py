@@ -281,6 +281,49 @@ def test_adamw_skip_leaves_state_untouched(zs):
         assert same_bits(from_dev(got, want.dtype == np.uint16), want)
 
 
+@pytest.mark.timeout(600)
+def test_adamw_and_pack_past_2_32_elements(zs):
+    """64-bit indexing: one AdamW step and the MXFP8 pack on n > 2^32
+    elements (about 78 GB of state), sampled around the 2^31 and 2^32
+    element boundaries and the ragged end."""
+    import torch
+    n = (1 << 32) + 4096 + 32 * 3
+    gspec = synth.make_spec(seed=1, cfg=55, stream=1, sigma=1e-3)
+    mspec = synth.make_spec(seed=1, cfg=55, stream=0, sigma=0.02)
+    g = torch.empty(n, dtype=torch.float32, device="cuda")
+    master = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.fill_device(gspec, 0, g)
+    synth.fill_device(mspec, 0, master)
+    m = torch.zeros(n, dtype=torch.float32, device="cuda")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda")
+    param = torch.empty(n, dtype=torch.int16, device="cuda")
+    elem = torch.empty(n, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+    zs.zero_adamw_step(master, m, v, grad_f32=g, step=1, lr=1e-3, weight_decay=0.01,
+                       param_bf16=param, mx_elem_out=elem, mx_scale_out=scale)
+    acc = zs.new_norm_acc(1)
+    with pytest.raises(zs.ZeroStepError):
+        zs.zero_grad_norm(g, 1.0, acc)                       # n >= 2^32: ESIZE
+    torch.cuda.synchronize()
+    blocks = np.array([0, (1 << 26) - 1, 1 << 26, (1 << 27) - 1, 1 << 27, n // 32 - 1],
+                      dtype=np.int64)
+    idx = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    di = torch.from_numpy(idx).cuda()
+    hg = synth.gather(gspec, idx.astype(np.uint64), False)
+    hmaster = synth.gather(mspec, idx.astype(np.uint64), False)
+    hm, hv = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
+    hparam = np.zeros(idx.size, np.uint16)
+    O.adamw(hg, 1.0, O.make_scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, 1), hmaster, hm, hv, hparam)
+    we, ws = O.mxfp8_pack(hparam)
+    assert same_bits(from_dev(master[di]), hmaster)
+    assert same_bits(from_dev(m[di]), hm) and same_bits(from_dev(v[di]), hv)
+    assert same_bits(from_dev(param[di], True), hparam)
+    assert np.array_equal(from_dev(elem[di]), we)
+    assert np.array_equal(from_dev(scale[torch.from_numpy(blocks).cuda()]), ws)
+    del g, master, m, v, param, elem, scale
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------- MXFP8 --
 
 def test_mxfp8_all_patterns_and_blocks(zs):
