@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements of the CPU-oracle sample")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip timing the unfused single-operation chain")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM "
                          "byte counters)")
@@ -85,6 +87,23 @@ def per_elem_bytes(w, st):
         else:
             kinds["mxfp8_pack"] = 2 + MX_BYTES
     return kinds
+
+
+def unfused_bytes(w):
+    """HBM bytes per element of the single-operation chain: every operation
+    reads its operands from HBM and writes its result back."""
+    b = w.P * w.g_bytes + 4      # s = sum of replicas
+    b += 4 + 4                   # g = s * inv_scale
+    b += 4                       # norm state of g
+    b += 4 + 4                   # g' = g * coef
+    b += 8 + 4                   # m
+    b += 8 + 4                   # v
+    b += 8 + 4                   # u = m / (sqrt(v)/sqrt_bc2 + eps)
+    b += 8 + 4                   # master
+    b += 4 + 2                   # bf16 param
+    if w.pack:
+        b += 2 + MX_BYTES        # MXFP8 pack of the param
+    return b
 
 
 def _read_counters(d):
@@ -276,6 +295,25 @@ def main():
         standalone["mxfp8_pack"] = {"avg_ms": round(ms, 4), "bytes_per_elem": 2 + MX_BYTES,
                                     "gbps": round((2 + MX_BYTES) * w.S / (ms * 1e-3) / 1e9, 1)}
 
+    unfused = None
+    if not args.no_unfused:
+        # The same step as a chain of single-operation kernels, same process
+        # and buffers: what fusion saves (bit-identical results).
+        for _ in range(max(1, args.warmup)):
+            st.step_unfused(reps)
+        torch.cuda.synchronize()
+        u0 = time.perf_counter()
+        for _ in range(args.steps):
+            st.step_unfused(reps)
+        torch.cuda.synchronize()
+        u_ms = 1e3 * (time.perf_counter() - u0) / args.steps
+        ub = unfused_bytes(w)
+        unfused = {"ms_per_step": round(u_ms, 4), "bytes_per_param": ub,
+                   "hbm_gbps": round(ub * w.S / (u_ms * 1e-3) / 1e9, 1),
+                   "launches_per_step": 11 + (1 if w.pack else 0),
+                   "fused_speedup": round(u_ms / (1e3 * elapsed / args.steps), 3)}
+        st.applied_steps()
+
     ms_per_step = 1e3 * elapsed / args.steps
     step_bytes = sum(kinds.values()) * w.S
     params_per_s = w.S / (elapsed / args.steps)
@@ -319,6 +357,7 @@ def main():
         "applied_steps": applied,
         "kernels": per_kernel,
         "standalone_kernels": standalone,
+        "unfused_chain": unfused,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),

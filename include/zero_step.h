@@ -189,6 +189,25 @@ int zero_step_gate(const zero_norm_acc *accs, int n_accs, double max_norm,
 int zero_mxfp8_pack(const uint16_t *bf16_in, size_t n, uint8_t *elem_out,
                     uint8_t *scale_out, void *stream);
 
+/* The same step as zero_shard_reduce (with its norm state) followed by
+ * zero_adamw_step, computed as a chain of single-operation passes, each its
+ * own kernel reading its operands from HBM and writing its result back:
+ * s = sum of replicas; g = s * inv_scale; norm state of g; gate; g' = g*coef;
+ * m; v; u = m / (sqrt(v)/sqrt_bc2 + eps); master; bf16 param; MXFP8 pack.
+ * This is the unfused baseline of Zero_From_Scratch's outline item on the
+ * trips to memory of an unfused chain: the results are bit for bit those of
+ * the fused path, only the HBM traffic and launches differ.
+ *   args       as for zero_adamw_step, except that `accs`/`n_accs` hold
+ *              only the OTHER ranks' accumulators (this rank's own norm is
+ *              computed inside the chain), and MXFP8 outputs need
+ *              param_bf16.
+ *   workspace  device scratch of at least zero_unfused_workspace_bytes(n,
+ *              n_accs) bytes, 256-byte aligned; contents are overwritten.
+ * ZERO_ESIZE if workspace_bytes is too small. */
+size_t zero_unfused_workspace_bytes(size_t n, int n_accs);
+int zero_adamw_step_unfused(const zero_adamw_args *args, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 int zero_abi_version(void);
 const char *zero_strerror(int status);
 

@@ -80,3 +80,8 @@ def test_argument_checks(lib):
     assert lib.zero_norm_acc_clear(None, 1, None) == -1
     assert lib.zero_norm_acc_clear(fake + 8, 1, None) == -2
     assert lib.zero_norm_acc_clear(None, 0, None) == 0
+    lib.zero_unfused_workspace_bytes.restype = C.c_size_t
+    lib.zero_unfused_workspace_bytes.argtypes = [C.c_size_t, C.c_int]
+    assert lib.zero_unfused_workspace_bytes(1000, 2) >= 2 * 4000 + 3 * 64
+    lib.zero_adamw_step_unfused.argtypes = [vp, vp, C.c_size_t, vp]
+    assert lib.zero_adamw_step_unfused(None, fake, 1 << 20, None) == -1

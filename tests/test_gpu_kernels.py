@@ -256,6 +256,33 @@ def test_adamw_fused_mxfp8_epilogue(zs):
         assert np.array_equal(from_dev(elem), want_e), n
 
 
+def test_binding_rejects_short_buffers(zs):
+    """The C ABI takes raw pointers; the binding refuses any buffer shorter
+    than the elements a call would touch (no launch happens)."""
+    import torch
+    n = 4096
+    f = lambda k: torch.zeros(k, dtype=torch.float32, device="cuda")
+    h = lambda k: torch.zeros(k, dtype=torch.int16, device="cuda")
+    u8 = lambda k: torch.zeros(k, dtype=torch.uint8, device="cuda")
+    kw = dict(step=1, lr=1e-3)
+    for bad in (dict(param_bf16=h(n - 1)), dict(mx_elem_out=u8(n - 1), mx_scale_out=u8(n // 32)),
+                dict(mx_elem_out=u8(n), mx_scale_out=u8(n // 32 - 1))):
+        with pytest.raises(ValueError):
+            zs.zero_adamw_step(f(n), f(n), f(n), grad_f32=f(n), **kw, **bad)
+    with pytest.raises(ValueError):
+        zs.zero_adamw_step(f(n), f(n), f(n), grad_f32=f(n - 8), **kw)
+    with pytest.raises(ValueError):
+        zs.zero_adamw_step(f(n), f(n), f(n), replicas=[h(n), h(n - 1)], **kw)
+    with pytest.raises(ValueError):
+        zs.zero_adamw_step(f(n), f(n), f(n), grad_f32=f(n), n=n + 1, **kw)
+    with pytest.raises(ValueError):
+        zs.zero_shard_reduce([h(n), h(n)], 0.5, g_out=f(n - 1))
+    with pytest.raises(ValueError):
+        zs.zero_grad_norm(h(n), 1.0, zs.new_norm_acc(1), n=n + 32)
+    with pytest.raises(ValueError):
+        zs.zero_mxfp8_pack(h(n), u8(n), u8(n // 32 - 1))
+
+
 def test_adamw_skip_leaves_state_untouched(zs):
     import torch
     n, P = 4096 + 3, 4
@@ -322,6 +349,47 @@ def test_adamw_and_pack_past_2_32_elements(zs):
     assert np.array_equal(from_dev(scale[torch.from_numpy(blocks).cuda()]), ws)
     del g, master, m, v, param, elem, scale
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("P,bf16", [(1, True), (3, True), (4, False), (8, True)])
+def test_unfused_chain_equals_fused_and_oracle(zs, P, bf16):
+    """The single-operation chain gives bit for bit the fused result (and the
+    oracle's), including the clip, a skipped call and the MXFP8 pack."""
+    import torch
+    for n, pack in ((4096 + 32 * 5, True), (33331, False)):
+        kw = dict(lr=1e-3, weight_decay=0.01, max_norm=0.05, check_overflow=True, pack=pack)
+        gdt = torch.bfloat16 if bf16 else torch.float32
+        fused = zs.ShardStep(n, P, gdt, **kw)
+        chain = zs.ShardStep(n, P, gdt, **kw)
+        ms = synth.make_spec(seed=n, cfg=56, stream=0, sigma=0.02)
+        master = synth.fill(ms, 0, n, False)
+        m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        param = O.f32_to_bf16(master)
+        for st in (fused, chain):
+            st.master.copy_(to_dev(master))
+            st.param.copy_(to_dev(param))
+        t = 0
+        for call in (1, 2, 3):
+            inject = [(P - 1, n // 2, np.inf)] if call == 2 else []
+            reps = _replicas(P, n, bf16, seed=500 * call + n, inject=inject)
+            dreps = [to_dev(r) for r in reps]
+            fused.step(dreps)
+            chain.step_unfused(dreps)
+            skipped, _ = O.step(reps, O.inv_scale(P, 1.0), 0.05, True, 1e-3, 0.9, 0.999, 1e-8,
+                                0.01, t + 1, master, m, v, param)
+            t += 0 if skipped else 1
+        torch.cuda.synchronize()
+        assert fused.applied_steps() == chain.applied_steps() == t == 2
+        for name, want in (("master", master), ("m", m), ("v", v), ("param", param)):
+            gf = from_dev(getattr(fused, name), name == "param")
+            gc = from_dev(getattr(chain, name), name == "param")
+            assert same_bits(gc, want), mismatch_report(f"unfused {name} n={n}", gc, want)
+            assert same_bits(gf, gc), name
+        if pack:
+            want_e, want_s = O.mxfp8_pack(param)
+            for st in (fused, chain):
+                assert np.array_equal(from_dev(st.mx_elem), want_e)
+                assert np.array_equal(from_dev(st.mx_scale), want_s)
 
 
 # ----------------------------------------------------------------- MXFP8 --

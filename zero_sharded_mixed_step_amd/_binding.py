@@ -57,8 +57,12 @@ def lib():
         L.zero_adamw_step.argtypes = [C.POINTER(_AdamArgs), vp]
         L.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
         L.zero_mxfp8_pack.argtypes = [vp, sz, vp, vp, vp]
+        L.zero_unfused_workspace_bytes.argtypes = [sz, i]
+        L.zero_unfused_workspace_bytes.restype = sz
+        L.zero_adamw_step_unfused.argtypes = [C.POINTER(_AdamArgs), vp, sz, vp]
         for f in (L.zero_norm_acc_clear, L.zero_shard_reduce, L.zero_grad_norm,
-                  L.zero_adamw_step, L.zero_step_gate, L.zero_mxfp8_pack):
+                  L.zero_adamw_step, L.zero_step_gate, L.zero_mxfp8_pack,
+                  L.zero_adamw_step_unfused):
             f.restype = i
         _lib = L
     return _lib
@@ -85,6 +89,23 @@ def _dev_ptr(t, name):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return C.c_void_p(t.data_ptr())
+
+
+def _need(t, n, name, dtypes):
+    """Every buffer a kernel touches must hold the elements it will touch:
+    the C ABI takes raw pointers, so lengths are checked here, before launch."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call touches {n}")
+
+
+F32 = (torch.float32,)
+BITS16 = (torch.bfloat16, torch.int16, torch.uint16)
+U8 = (torch.uint8,)
+I32 = (torch.int32,)
 
 
 def _dtype_code(t):
@@ -156,10 +177,10 @@ def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
         raise ValueError("at least one replica")
     n = reps[0].numel() if n is None else int(n)
     for r in reps:
-        if r.numel() < n or r.dtype != reps[0].dtype:
-            raise ValueError("replicas must share dtype and hold n elements")
-    if g_out is not None and (g_out.dtype != torch.float32 or g_out.numel() < n):
-        raise ValueError("g_out must be float32 with n elements")
+        if r.dtype != reps[0].dtype:
+            raise ValueError("replicas must share one dtype")
+        _need(r, n, "replica", F32 + BITS16)
+    _need(g_out, n, "g_out", F32)
     ap, k = _acc_ptr(acc)
     if k > 1:
         raise ValueError("zero_shard_reduce adds to one accumulator")
@@ -170,6 +191,7 @@ def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
 
 def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:
     n = grad.numel() if n is None else int(n)
+    _need(grad, n, "grad", F32 + BITS16)
     ap, k = _acc_ptr(acc)
     if k != 1:
         raise ValueError("zero_grad_norm adds to one accumulator")
@@ -177,17 +199,21 @@ def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:
                                 float(inv_scale), ap, _stream(stream)), "zero_grad_norm")
 
 
-def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
-                    weight_decay=0.0, grad_f32=None, replicas=None, inv_scale=1.0,
-                    param_bf16=None, accs=None, max_norm=0.0, check_overflow=False,
-                    skipped_out=None, mx_elem_out=None, mx_scale_out=None, n=None,
-                    stream=None) -> None:
+def _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32, replicas,
+               inv_scale, param_bf16, accs, max_norm, check_overflow, skipped_out, mx_elem_out,
+               mx_scale_out, n):
     n = master.numel() if n is None else int(n)
-    for name, t in (("m", m), ("v", v)):
-        if t.numel() < n or t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32 with n elements")
-    if master.dtype != torch.float32:
-        raise ValueError("master must be float32")
+    for name, t in (("master", master), ("m", m), ("v", v), ("grad_f32", grad_f32)):
+        _need(t, n, name, F32)
+    if replicas is not None:
+        for r in replicas:
+            if r.dtype != replicas[0].dtype:
+                raise ValueError("replicas must share one dtype")
+            _need(r, n, "replica", F32 + BITS16)
+    _need(param_bf16, n, "param_bf16", BITS16)
+    _need(skipped_out, 1, "skipped_out", I32)
+    _need(mx_elem_out, n, "mx_elem_out", U8)
+    _need(mx_scale_out, n // 32, "mx_scale_out", U8)
     a = _AdamArgs()
     a.n = n
     keep = None
@@ -213,12 +239,47 @@ def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
     a.skipped_out = _dev_ptr(skipped_out, "skipped_out")
     a.mx_elem_out = _dev_ptr(mx_elem_out, "mx_elem_out")
     a.mx_scale_out = _dev_ptr(mx_scale_out, "mx_scale_out")
+    return a, keep
+
+
+def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                    weight_decay=0.0, grad_f32=None, replicas=None, inv_scale=1.0,
+                    param_bf16=None, accs=None, max_norm=0.0, check_overflow=False,
+                    skipped_out=None, mx_elem_out=None, mx_scale_out=None, n=None,
+                    stream=None) -> None:
+    a, keep = _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32,
+                         replicas, inv_scale, param_bf16, accs, max_norm, check_overflow,
+                         skipped_out, mx_elem_out, mx_scale_out, n)
     rc = lib().zero_adamw_step(C.byref(a), _stream(stream))
     del keep
     _check(rc, "zero_adamw_step")
 
 
+def zero_unfused_workspace_bytes(n: int, n_accs: int = 0) -> int:
+    return lib().zero_unfused_workspace_bytes(int(n), int(n_accs))
+
+
+def zero_adamw_step_unfused(master, m, v, workspace, *, step, lr, beta1=0.9, beta2=0.999,
+                            eps=1e-8, weight_decay=0.0, grad_f32=None, replicas=None,
+                            inv_scale=1.0, param_bf16=None, accs=None, max_norm=0.0,
+                            check_overflow=False, skipped_out=None, mx_elem_out=None,
+                            mx_scale_out=None, n=None, stream=None) -> None:
+    """The step as a chain of single-operation kernels (`accs`: the OTHER
+    ranks' accumulators; `workspace`: a uint8 device tensor of at least
+    zero_unfused_workspace_bytes(n, k) bytes)."""
+    a, keep = _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32,
+                         replicas, inv_scale, param_bf16, accs, max_norm, check_overflow,
+                         skipped_out, mx_elem_out, mx_scale_out, n)
+    rc = lib().zero_adamw_step_unfused(C.byref(a), _dev_ptr(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    del keep
+    _check(rc, "zero_adamw_step_unfused")
+
+
 def zero_step_gate(accs, max_norm, check_overflow, coef_out, skip_out, stream=None) -> None:
+    _need(coef_out, 1, "coef_out", F32)
+    _need(skip_out, 1, "skip_out", I32)
     ap, k = _acc_ptr(accs)
     _check(lib().zero_step_gate(ap, k, float(max_norm), int(bool(check_overflow)),
                                 _dev_ptr(coef_out, "coef_out"), _dev_ptr(skip_out, "skip_out"),
@@ -227,6 +288,9 @@ def zero_step_gate(accs, max_norm, check_overflow, coef_out, skip_out, stream=No
 
 def zero_mxfp8_pack(x_bf16, elem_out, scale_out, n=None, stream=None) -> None:
     n = x_bf16.numel() if n is None else int(n)
+    _need(x_bf16, n, "x_bf16", BITS16)
+    _need(elem_out, n, "elem_out", U8)
+    _need(scale_out, n // 32, "scale_out", U8)
     _check(lib().zero_mxfp8_pack(_dev_ptr(x_bf16, "x"), n, _dev_ptr(elem_out, "elem_out"),
                                  _dev_ptr(scale_out, "scale_out"), _stream(stream)),
            "zero_mxfp8_pack")

@@ -127,47 +127,84 @@ int zero_grad_norm(const void* grad, int dtype, size_t n, float inv_scale, zero_
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks of zero_adamw_args; fills the launch description.
+int adamw_args_to_launch(const zero_adamw_args* a, zs::AdamLaunch& L) {
+  if (a == nullptr) return ZERO_EINVAL;
+  if (a->master == nullptr || a->m == nullptr || a->v == nullptr) return ZERO_EINVAL;
+  if ((a->grad_f32 == nullptr) == (a->replicas == nullptr)) return ZERO_EINVAL;
+  if (a->step < 1 || a->n_accs < 0 || (a->n_accs > 0 && a->accs == nullptr)) return ZERO_EINVAL;
+  if (a->replicas != nullptr) {
+    const int rc = check_replicas(a->replicas, a->P, a->dtype);
+    if (rc != ZERO_OK) return rc;
+  }
+  if (!aligned16(a->master) || !aligned16(a->m) || !aligned16(a->v) ||
+      (a->grad_f32 && !aligned16(a->grad_f32)) ||
+      (a->param_bf16 && !aligned16(a->param_bf16)) || (a->accs && !aligned16(a->accs)) ||
+      (a->skipped_out && !aligned4(a->skipped_out)) ||
+      (a->mx_elem_out && !aligned16(a->mx_elem_out)) ||
+      (a->mx_scale_out && !aligned16(a->mx_scale_out)))
+    return ZERO_EALIGN;
+  if ((a->mx_elem_out == nullptr) != (a->mx_scale_out == nullptr)) return ZERO_EINVAL;
+  if (a->mx_elem_out != nullptr && a->n % 32 != 0) return ZERO_ESIZE;
+  L.grad = a->grad_f32;
+  L.replicas = a->replicas;
+  L.P = a->replicas ? a->P : 1;
+  L.dtype = a->dtype;
+  L.inv_scale = a->inv_scale;
+  L.master = a->master;
+  L.m = a->m;
+  L.v = a->v;
+  L.param = a->param_bf16;
+  L.mx_elem = a->mx_elem_out;
+  L.mx_scale = a->mx_scale_out;
+  L.accs = a->n_accs > 0 ? a->accs : nullptr;
+  L.n_accs = a->n_accs;
+  L.max_norm = a->max_norm;
+  L.check_overflow = a->check_overflow;
+  L.skipped_out = a->skipped_out;
+  L.n = a->n;
+  L.s = derive_scalars(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
+  return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int zero_adamw_step(const zero_adamw_args* a, void* stream) {
   try {
-    if (a == nullptr) return ZERO_EINVAL;
-    if (a->master == nullptr || a->m == nullptr || a->v == nullptr) return ZERO_EINVAL;
-    if ((a->grad_f32 == nullptr) == (a->replicas == nullptr)) return ZERO_EINVAL;
-    if (a->step < 1 || a->n_accs < 0 || (a->n_accs > 0 && a->accs == nullptr))
-      return ZERO_EINVAL;
-    if (a->replicas != nullptr) {
-      const int rc = check_replicas(a->replicas, a->P, a->dtype);
-      if (rc != ZERO_OK) return rc;
-    }
-    if (!aligned16(a->master) || !aligned16(a->m) || !aligned16(a->v) ||
-        (a->grad_f32 && !aligned16(a->grad_f32)) ||
-        (a->param_bf16 && !aligned16(a->param_bf16)) || (a->accs && !aligned16(a->accs)) ||
-        (a->skipped_out && !aligned4(a->skipped_out)) ||
-        (a->mx_elem_out && !aligned16(a->mx_elem_out)) ||
-        (a->mx_scale_out && !aligned16(a->mx_scale_out)))
-      return ZERO_EALIGN;
-    if ((a->mx_elem_out == nullptr) != (a->mx_scale_out == nullptr)) return ZERO_EINVAL;
-    if (a->mx_elem_out != nullptr && a->n % 32 != 0) return ZERO_ESIZE;
     zs::AdamLaunch L;
-    L.grad = a->grad_f32;
-    L.replicas = a->replicas;
-    L.P = a->replicas ? a->P : 1;
-    L.dtype = a->dtype;
-    L.inv_scale = a->inv_scale;
-    L.master = a->master;
-    L.m = a->m;
-    L.v = a->v;
-    L.param = a->param_bf16;
-    L.mx_elem = a->mx_elem_out;
-    L.mx_scale = a->mx_scale_out;
-    L.accs = a->n_accs > 0 ? a->accs : nullptr;
-    L.n_accs = a->n_accs;
-    L.max_norm = a->max_norm;
-    L.check_overflow = a->check_overflow;
-    L.skipped_out = a->skipped_out;
-    L.n = a->n;
-    L.s = derive_scalars(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
+    const int rc = adamw_args_to_launch(a, L);
+    if (rc != ZERO_OK) return rc;
     if (a->n == 0 && a->skipped_out == nullptr) return ZERO_OK;
     return status_of(zs::launch_adamw(L, as_stream(stream)));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
+size_t zero_unfused_workspace_bytes(size_t n, int n_accs) {
+  return static_cast<size_t>(zs::unfused_workspace_bytes(n, n_accs < 0 ? 0 : n_accs));
+}
+
+int zero_adamw_step_unfused(const zero_adamw_args* a, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  try {
+    zs::AdamLaunch L;
+    const int rc = adamw_args_to_launch(a, L);
+    if (rc != ZERO_OK) return rc;
+    if (a->mx_elem_out != nullptr && a->param_bf16 == nullptr) return ZERO_EINVAL;
+    if (a->n >= (size_t(1) << 32)) return ZERO_ESIZE;  // the chain's own norm accumulator
+    if (workspace == nullptr) return ZERO_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ZERO_EALIGN;
+    if (workspace_bytes < zs::unfused_workspace_bytes(a->n, a->n_accs)) return ZERO_ESIZE;
+    if (a->n == 0) return ZERO_OK;
+    return status_of(
+        zs::launch_unfused(L, L.accs, L.n_accs, workspace, as_stream(stream)));
   } catch (...) {
     return ZERO_EHIP;
   }

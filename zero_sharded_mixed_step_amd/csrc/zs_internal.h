@@ -62,7 +62,13 @@ hipError_t launch_gate(const zero_norm_acc* accs, int n_accs, double max_norm,
 
 hipError_t launch_acc_clear(zero_norm_acc* accs, int n_accs, hipStream_t stream);
 
+struct Gate;
 hipError_t launch_mxfp8(const uint16_t* in, uint64_t n, uint8_t* elem, uint8_t* scale,
-                        hipStream_t stream);
+                        hipStream_t stream, const Gate* gate = nullptr);
+
+// The unfused chain (zs_unfused.hip): the step as single-operation passes.
+uint64_t unfused_workspace_bytes(uint64_t n, int n_other_accs);
+hipError_t launch_unfused(const AdamLaunch& a, const zero_norm_acc* other_accs,
+                          int n_other_accs, void* workspace, hipStream_t stream);
 
 }  // namespace zs

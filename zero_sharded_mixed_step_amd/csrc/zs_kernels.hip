@@ -54,7 +54,7 @@ struct ReduceParams {
 };
 
 #ifndef ZS_REDUCE_LOADS
-#define ZS_REDUCE_LOADS 32
+#define ZS_REDUCE_LOADS 24
 #endif
 
 
@@ -466,7 +466,9 @@ hipError_t launch_acc_clear(zero_norm_acc* accs, int n_accs, hipStream_t stream)
 // ZS_MX_UNROLL tiles per iteration, so that several 16-byte loads per lane
 // are in flight before the integer encoding starts.
 __global__ void __launch_bounds__(kThreads) mxfp8_kernel(const uint16_t* in, uint64_t nchunks,
-                                                         uint8_t* elem, uint8_t* scale) {
+                                                         uint8_t* elem, uint8_t* scale,
+                                                         const Gate* gate) {
+  if (gate != nullptr && gate->skip) return;  // a skipped step writes nothing
   const uint64_t ntiles = (nchunks + kThreads - 1) / kThreads;
   constexpr int U = ZS_MX_UNROLL;
   for (uint64_t tile = static_cast<uint64_t>(blockIdx.x) * U; tile < ntiles;
@@ -497,11 +499,11 @@ __global__ void __launch_bounds__(kThreads) mxfp8_kernel(const uint16_t* in, uin
 }
 
 hipError_t launch_mxfp8(const uint16_t* in, uint64_t n, uint8_t* elem, uint8_t* scale,
-                        hipStream_t stream) {
+                        hipStream_t stream, const Gate* gate) {
   const uint64_t nchunks = n / kVec;
   const unsigned grid = grid_for(nchunks, ZS_PACK_BLOCKS_PER_CU);
   hipLaunchKernelGGL(mxfp8_kernel, dim3(grid), dim3(kThreads), 0, stream, in, nchunks, elem,
-                     scale);
+                     scale, gate);
   return hipGetLastError();
 }
 

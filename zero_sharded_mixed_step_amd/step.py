@@ -155,6 +155,33 @@ class ShardStep:
         if self.pack and not self.fuse_pack:
             self.pack_param()
 
+    def step_unfused(self, replicas: List[torch.Tensor],
+                     other_accs: Optional[torch.Tensor] = None) -> None:
+        """The same step as `step`, as the chain of single-operation kernels
+        (one HBM round trip per operation): the unfused baseline.  Results are
+        bit for bit those of `step`."""
+        need = B.zero_unfused_workspace_bytes(
+            self.n, 0 if other_accs is None else other_accs.numel() // B.ACC_WORDS)
+        ws = getattr(self, "_unfused_ws", None)
+        if ws is None or ws.numel() < need:
+            ws = self._unfused_ws = torch.empty(need, dtype=torch.uint8, device=self.master.device)
+        self._resolve_pending_skip()
+        kw = dict(step=self.t + 1, lr=self.lr, beta1=self.beta1, beta2=self.beta2,
+                  eps=self.eps, weight_decay=self.wd, param_bf16=self.param,
+                  max_norm=self.max_norm, check_overflow=self.check_overflow,
+                  replicas=replicas, inv_scale=self.inv_scale, accs=other_accs)
+        if self.check_overflow:
+            kw["skipped_out"] = self.skipped
+        if self.pack:
+            kw["mx_elem_out"], kw["mx_scale_out"] = self.mx_elem, self.mx_scale
+        B.zero_adamw_step_unfused(self.master, self.m, self.v, ws, **kw)
+        if self.check_overflow:
+            self._skip_host.copy_(self.skipped, non_blocking=True)
+            self._skip_event = torch.cuda.Event()
+            self._skip_event.record()
+        else:
+            self.t += 1
+
     def applied_steps(self) -> int:
         """Applied updates so far (waits for the last skip flag)."""
         self._resolve_pending_skip()
