@@ -95,6 +95,8 @@ def _load(path):
     L.oracle_mxfp8_pack.restype = C.c_int
     L.oracle_e4m3_value.argtypes = [C.c_uint8]
     L.oracle_e4m3_value.restype = C.c_double
+    L.oracle_mxfp8_decode.argtypes = [vp, vp, sz, vp]
+    L.oracle_mxfp8_decode.restype = C.c_int
     return L
 
 
@@ -255,3 +257,15 @@ def mxfp8_pack(x: np.ndarray):
     rc = lib().oracle_mxfp8_pack(_ptr(x), n, _ptr(elem), _ptr(scale))
     assert rc == 0
     return elem, scale
+
+
+def mxfp8_decode(elem: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    elem = np.ascontiguousarray(elem, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint8)
+    n = elem.size
+    if n % 32 or scale.size < n // 32:
+        raise ValueError("MXFP8 decode needs n % 32 == 0 and n/32 scales")
+    out = np.empty(n, dtype=np.float32)
+    rc = lib().oracle_mxfp8_decode(_ptr(elem), _ptr(scale), n, _ptr(out))
+    assert rc == 0
+    return out

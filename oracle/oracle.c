@@ -362,3 +362,19 @@ double oracle_e4m3_value(uint8_t code) {
   if (ex == 0) return sign * ldexp((double)mt, -9);
   return sign * ldexp(8.0 + mt, ex - 7 - 3);
 }
+
+int oracle_mxfp8_decode(const uint8_t *elem, const uint8_t *scale, size_t n,
+                        float *out) {
+  if (n % 32 != 0) return -1;
+  for (size_t i = 0; i < n; ++i) {
+    uint8_t code = elem[i];
+    uint8_t sb = scale[i / 32];
+    double val = oracle_e4m3_value(code);
+    if (sb == 0xFF || isnan(val)) {
+      out[i] = (code & 0x80) ? -NAN : NAN;
+      continue;
+    }
+    out[i] = (float)ldexp(val, (int)sb - 127);
+  }
+  return 0;
+}

@@ -139,6 +139,13 @@ int oracle_mxfp8_pack(const uint16_t *x, size_t n, uint8_t *elem,
                       uint8_t *scale);
 double oracle_e4m3_value(uint8_t code);
 
+/* MXFP8 decode: element i of a packed vector is e4m3_value(elem[i]) *
+ * 2^(scale[i/32] - 127), rounded once to binary32 (exact except where the
+ * product overflows binary32); scale byte 0xFF (NaN) or a NaN code give a
+ * NaN with the code's sign.  n % 32 == 0, else -1. */
+int oracle_mxfp8_decode(const uint8_t *elem, const uint8_t *scale, size_t n,
+                        float *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -598,6 +598,54 @@ def check_mx_block_properties():
                                                        2.0 ** (e_s - 10)) + 64 * 2.0 ** e_s)
 
 
+def check_mx_decode_vs_torch_fp8():
+    # Element values from torch's float8_e4m3fn (a library routine), scaled
+    # by 2^(scale-127) exactly in binary64 and rounded once to binary32.
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().double().numpy()
+    for sb in list(range(0, 256, 7)) + [1, 126, 127, 128, 254, 255]:
+        elem = np.tile(codes, 1)
+        scale = np.full(256 // 32, sb, np.uint8)
+        got = O.mxfp8_decode(elem, scale)
+        if sb == 0xFF:
+            assert np.isnan(got).all()
+            continue
+        want = np.ldexp(ref, sb - 127).astype(np.float32)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), sb
+        assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32)), sb
+        assert np.array_equal(np.signbit(got[nan]), codes[nan] >= 0x80)
+
+
+def check_mx_decode_golden_and_roundtrip():
+    for b in golden("mxfp8_blocks.json")["blocks"]:
+        if b["scale"] in ("0xFF",):
+            continue
+        fill = hx(b.get("fill", "0x0000"))
+        blk = np.full(32, fill, np.uint16)
+        blk[:len(b["bf16"])] = [hx(v) for v in b["bf16"]]
+        elem, scale = O.mxfp8_pack(blk)
+        dec = O.mxfp8_decode(elem, scale).astype(np.float64)
+        x = (blk.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        e_s = int(scale[0]) - 127
+        # each element decodes to within half an E4M3 step of its input, or to
+        # +-448 * 2^e_s when it saturated
+        step = np.where(np.abs(x) < 2.0 ** (e_s - 6), 2.0 ** (e_s - 9),
+                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-300))) - 3))
+        sat = np.abs(x) >= 448 * 2.0 ** e_s
+        ok = np.where(sat, np.abs(dec) == 448 * 2.0 ** e_s, np.abs(dec - x) <= step / 2)
+        assert ok.all(), (b, dec[:4], x[:4])
+    # hand values: 1.0, 0.94140625, 0.96875, 0.90625 under scale byte 119
+    elem = np.zeros(32, np.uint8)
+    elem[:4] = [0x78, 0x77, 0x78, 0x76]
+    dec = O.mxfp8_decode(elem, np.array([0x77], np.uint8))
+    assert list(dec[:4]) == [1.0, 0.9375, 1.0, 0.875]
+    # subnormal codes at the smallest scale: 3 * 2^-9 * 2^-127 = 3 * 2^-136
+    dec = O.mxfp8_decode(np.full(32, 0x83, np.uint8), np.array([0], np.uint8))
+    assert dec[0] == -3 * 2.0 ** -136
+
+
 def check_mx_sizes():
     # Bytes per weight: bf16 2, MXFP8 1 + 1/32.  Stored state of 16 B per
     # weight with param and grad in MXFP8 shrinks by 12.1 %, and an

@@ -63,6 +63,9 @@ MUTANTS = [
     ("mx_scale_no_clamp", "if (e_s < -127) e_s = -127;", "(void)0;"),
     ("mx_zero_block_scale", "      scale[b] = 0x00;\n", "      scale[b] = 0x7F;\n"),
     ("mx_inf_not_special", "if (!isfinite(val))", "if (isnan(val))"),
+    ("mx_decode_bias", "out[i] = (float)ldexp(val, (int)sb - 127);", "out[i] = (float)ldexp(val, (int)sb - 126);"),
+    ("mx_decode_nan_scale", "if (sb == 0xFF || isnan(val)) {", "if (isnan(val)) {"),
+    ("mx_decode_block_index", "uint8_t sb = scale[i / 32];", "uint8_t sb = scale[i / 16];"),
 ]
 
 
