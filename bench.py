@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="C5", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--config", default="C5", choices=["C1", "C2", "C3", "C4", "C5", "C5M"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements of the CPU-oracle sample")
@@ -73,7 +73,7 @@ MX_BYTES = 1 + 1.0 / 32        # MXFP8 codes + one scale byte per 32 elements
 def per_elem_bytes(w, st):
     """Fused-minimum HBM bytes per shard element, per launch kind.  With the
     MXFP8 pack fused into AdamW its output bytes belong to the AdamW pass."""
-    g_b = w.g_bytes
+    g_b = MX_BYTES if w.mx_grads else w.g_bytes
     P = w.P
     if st.path == "fused":
         kinds = {"adamw": P * g_b + 26}
@@ -188,11 +188,17 @@ def cpu_baseline(w, sample, steps):
     g_tmp = np.empty(sample, np.float32)
     reps = [synth.fill(w.grad_spec(1, k), start, sample, w.grad_bf16, threads=8)
             for k in range(w.P)]
+    if w.mx_grads:
+        sample = sample // 32 * 32
+        reps = [O.mxfp8_pack(r[:sample]) for r in reps]
+        master, m, v, param, g_tmp = (a[:sample] for a in (master, m, v, param, g_tmp))
     inv = O.inv_scale(w.P, w.loss_scale)
     elem = np.empty(sample, np.uint8) if w.pack else None
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
-        O.step(reps, inv, w.max_norm, w.check_overflow, w.lr, w.beta1, w.beta2, w.eps,
+        # MXFP8-stored replicas: the decode is part of the timed step
+        g_in = [O.mxfp8_decode(e, sc) for e, sc in reps] if w.mx_grads else reps
+        O.step(g_in, inv, w.max_norm, w.check_overflow, w.lr, w.beta1, w.beta2, w.eps,
                w.wd, t, master, m, v, param, g_tmp=g_tmp)
         if w.pack:
             elem, _ = O.mxfp8_pack(param[: sample // 32 * 32])
@@ -230,7 +236,8 @@ def main():
     w = configs.ALL[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    st = zs.ShardStep(w.S, w.P, torch.bfloat16 if w.grad_bf16 else torch.float32, lr=w.lr,
+    grad_dtype = "mxfp8" if w.mx_grads else (torch.bfloat16 if w.grad_bf16 else torch.float32)
+    st = zs.ShardStep(w.S, w.P, grad_dtype, lr=w.lr,
                       beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
                       max_norm=w.max_norm, check_overflow=w.check_overflow,
                       loss_scale=w.loss_scale, bucket=w.bucket, pack=w.pack, device=dev)
@@ -239,10 +246,22 @@ def main():
     synth.fill_device(w.master_spec(), start, st.param)
     gdt = torch.int16 if w.grad_bf16 else torch.float32
     reps = []
-    for k in range(w.P):
-        r = torch.empty(w.S, dtype=gdt, device=dev)
-        synth.fill_device(w.grad_spec(1, k), start, r)
-        reps.append(r)
+    if w.mx_grads:
+        # MXFP8-stored replicas: the bf16 replicas, packed on the device
+        tmp = torch.empty(w.S, dtype=gdt, device=dev)
+        for k in range(w.P):
+            synth.fill_device(w.grad_spec(1, k), start, tmp)
+            codes = torch.empty(w.S, dtype=torch.uint8, device=dev)
+            scales = torch.empty(w.S // 32, dtype=torch.uint8, device=dev)
+            zs.zero_mxfp8_pack(tmp, codes, scales)
+            reps.append((codes, scales))
+        torch.cuda.synchronize()
+        del tmp
+    else:
+        for k in range(w.P):
+            r = torch.empty(w.S, dtype=gdt, device=dev)
+            synth.fill_device(w.grad_spec(1, k), start, r)
+            reps.append(r)
     torch.cuda.synchronize()
 
     kinds = per_elem_bytes(w, st)
@@ -296,7 +315,7 @@ def main():
                                     "gbps": round((2 + MX_BYTES) * w.S / (ms * 1e-3) / 1e9, 1)}
 
     unfused = None
-    if not args.no_unfused:
+    if not args.no_unfused and not w.mx_grads:
         # The same step as a chain of single-operation kernels, same process
         # and buffers: what fusion saves (bit-identical results).
         for _ in range(max(1, args.warmup)):
@@ -347,7 +366,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.title}", "shard_elems": w.S, "P": w.P,
-                   "grad_dtype": "bf16" if w.grad_bf16 else "f32", "bucket": w.bucket,
+                   "grad_dtype": "mxfp8" if w.mx_grads else ("bf16" if w.grad_bf16 else "f32"),
+                   "bucket": w.bucket,
                    "max_norm": w.max_norm, "check_overflow": w.check_overflow,
                    "mxfp8_pack": ("fused into AdamW" if st.fuse_pack else "separate pass")
                    if w.pack else False, "path": st.path},

@@ -58,8 +58,10 @@ extern "C" {
 #define ZERO_ABI_VERSION 2
 #define ZERO_MAX_REPLICAS 64
 
-/* Element types of gradient replicas. */
-enum { ZERO_F32 = 0, ZERO_BF16 = 1 };
+/* Element types of gradient replicas.  ZERO_MXFP8 replicas (E4M3 codes plus
+ * one E8M0 scale byte per 32 elements) are accepted by zero_shard_reduce_mx
+ * only. */
+enum { ZERO_F32 = 0, ZERO_BF16 = 1, ZERO_MXFP8 = 2 };
 
 /* Status codes. */
 enum {
@@ -115,6 +117,24 @@ float zero_inv_scale(int P, double loss_scale);
 int zero_shard_reduce(const void *const *replicas, int P, int dtype, size_t n,
                       float inv_scale, float *g_out, zero_norm_acc *acc,
                       void *stream);
+
+/* Shard reduce of MXFP8-stored gradient replicas (the "12 percent off stored
+ * state" of Zero_From_Scratch's outline item on MXFP8: bf16 gradients kept
+ * as E4M3 codes plus one E8M0 scale per 32 elements, 1.03 instead of 2 bytes
+ * per element).  Each element decodes exactly to
+ *   x = e4m3_value(code) * 2^(scale - 127)   (binary32, exact; scale byte
+ *   0xFF or a NaN code gives NaN),
+ * then g[i] = (x_0[i] + ... + x_{P-1}[i]) * inv_scale exactly as
+ * zero_shard_reduce sums, with the same norm state.
+ *   codes[k]   HOST array of P device pointers to uint8[n] E4M3 codes
+ *              (16-byte aligned)
+ *   scales[k]  HOST array of P device pointers to uint8[n/32] scale bytes
+ *              (any alignment); for a bucket at element offset `lo` pass
+ *              codes + lo and scales + lo/32.
+ *   n % 32 == 0 (ZERO_ESIZE otherwise).  g_out / acc as zero_shard_reduce. */
+int zero_shard_reduce_mx(const uint8_t *const *codes, const uint8_t *const *scales,
+                         int P, size_t n, float inv_scale, float *g_out,
+                         zero_norm_acc *acc, void *stream);
 
 /* Norm state of one buffer: adds the groups of g[i] = grad[i] * inv_scale
  * (grad fp32 or bf16, device) to acc, as zero_shard_reduce with P = 1 and

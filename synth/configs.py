@@ -40,6 +40,7 @@ class Workload:
     master_sigma: float = 0.02
     bucket: Optional[int] = None
     pack: bool = False
+    mx_grads: bool = False      # replicas stored as MXFP8 (codes + E8M0 scales)
     inject: Optional[Tuple[int, int]] = None   # (1-based call, element)
     rank: int = 0
     cfg_id: int = 0
@@ -91,4 +92,11 @@ C5 = Workload("C5", "30B model ZeRO-3, rank-0 shard of 3.75B at P=8, 8 bf16 repl
               N=30_000_000_000, P=8, S=3_750_000_000, grad_bf16=True, grad_sigma=1e-3,
               steps=5, max_norm=1.0, check_overflow=True, pack=True, cfg_id=5)
 
-ALL = {w.name: w for w in (C1, C2, C3, C4, C5)}
+# The 30B shard with its gradient replicas stored as MXFP8 (the bf16
+# replicas of C5, packed), the stored-state saving of the pages' MXFP8 item.
+C5M = Workload("C5M", "30B model ZeRO-3, rank-0 shard of 3.75B at P=8, 8 MXFP8-stored grad "
+               "replicas, clip 1.0 + overflow check, 5 steps, MXFP8 param pack",
+               N=30_000_000_000, P=8, S=3_750_000_000, grad_bf16=True, grad_sigma=1e-3,
+               steps=5, max_norm=1.0, check_overflow=True, pack=True, mx_grads=True, cfg_id=5)
+
+ALL = {w.name: w for w in (C1, C2, C3, C4, C5, C5M)}

@@ -65,6 +65,8 @@ def oracle_norm_range(workload, call, lo, hi, chunk=1 << 21):
                 for k in range(P)]
         if workload.inject and workload.inject[0] == call and s <= workload.inject[1] < e:
             reps[0][workload.inject[1] - s] = 0x7F80 if workload.grad_bf16 else np.float32(np.inf)
+        if getattr(workload, "mx_grads", False):     # MXFP8-stored: pack, then decode
+            reps = [O.mxfp8_decode(*O.mxfp8_pack(r)) for r in reps]
         O.norm_accumulate(O.reduce(reps, inv), acc)
     return acc
 

@@ -42,12 +42,25 @@ def _step_for(zs, w, **over):
               bucket=w.bucket, pack=w.pack)
     kw.update(over)
     n = kw.pop("n", w.S)
-    return zs.ShardStep(n, w.P, torch.bfloat16 if w.grad_bf16 else torch.float32, **kw)
+    gdt = "mxfp8" if w.mx_grads else (torch.bfloat16 if w.grad_bf16 else torch.float32)
+    return zs.ShardStep(n, w.P, gdt, **kw)
 
 
 def _device_replicas(w, call, lo, n, out=None):
     import torch
     gdt = torch.int16 if w.grad_bf16 else torch.float32
+    if w.mx_grads:
+        # MXFP8-stored replicas: each bf16 replica packed on the device
+        import zero_sharded_mixed_step_amd as zs
+        if out is None:
+            out = [(torch.empty(n, dtype=torch.uint8, device="cuda"),
+                    torch.empty(n // 32, dtype=torch.uint8, device="cuda")) for _ in range(w.P)]
+        tmp = torch.empty(n, dtype=gdt, device="cuda")
+        for k, (codes, scales) in enumerate(out):
+            synth.fill_device(w.grad_spec(call, k), lo, tmp)
+            zs.zero_mxfp8_pack(tmp, codes, scales)
+        torch.cuda.synchronize()
+        return out
     if out is None:
         out = [torch.empty(n, dtype=gdt, device="cuda") for _ in range(w.P)]
     for k, r in enumerate(out):
@@ -149,7 +162,12 @@ def _sample_indices(w, rng, k=4096):
     if w.inject:
         marks += [w.inject[1] - 1, w.inject[1], w.inject[1] + 1]
     idx.update(i for i in marks if 0 <= i < S)
-    return np.array(sorted(idx), dtype=np.uint64)
+    idx = np.array(sorted(idx), dtype=np.uint64)
+    if w.mx_grads:
+        # whole 32-element blocks: a decoded element depends on its block
+        blocks = np.unique(idx // np.uint64(32))
+        idx = (blocks[:, None] * np.uint64(32) + np.arange(32, dtype=np.uint64)[None, :]).ravel()
+    return idx
 
 
 def _oracle_gates(w, calls):
@@ -178,6 +196,8 @@ def _oracle_samples(w, idx, calls, gates):
             hit = np.nonzero(gidx == np.uint64(w.inject[1]))[0]
             for h in hit:
                 reps[0][h] = 0x7F80 if w.grad_bf16 else np.float32(np.inf)
+        if w.mx_grads:      # idx holds whole blocks, in order
+            reps = [O.mxfp8_decode(*O.mxfp8_pack(r)) for r in reps]
         g = O.reduce(reps, inv)
         O.adamw(g, coef, O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, t), master, m,
                 v, param)
@@ -249,3 +269,14 @@ def test_30b_shard_clip_overflow_then_mxfp8(zs):
     for e, sc in ((fused_e, fused_s), (got_e, got_s)):
         assert np.array_equal(sc, want_s)
         assert np.array_equal(e, want_e)
+
+
+@pytest.mark.timeout(1200)
+def test_30b_shard_mxfp8_stored_grads(zs):
+    # 1 of the 5 steps at the full 3.75B shard: the host oracle packs and
+    # decodes all 8 replicas of the whole shard for the norm (~2 min on 16
+    # threads), so one call is what fits
+    w = configs.C5M
+    st, idx, gates = _run_sampled(zs, w, calls=range(1, 2), seed=6)
+    assert st.path == "materialize" and idx.size % 32 == 0
+    assert gates[0][1] is False

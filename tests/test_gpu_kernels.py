@@ -115,6 +115,110 @@ def test_buckets_and_grid_shapes_do_not_change_the_norm(zs):
         assert zs.read_norm_acc(acc) == zs.read_norm_acc(whole), bucket
 
 
+# ------------------------------------------------- MXFP8-stored replicas --
+
+def _same_or_both_nan(a: np.ndarray, b: np.ndarray) -> bool:
+    """Bitwise equal where finite or infinite; NaN exactly where the other is
+    NaN (the payload and sign of a NaN are not part of the result)."""
+    na, nb = np.isnan(a), np.isnan(b)
+    return a.shape == b.shape and np.array_equal(na, nb) and same_bits(a[~na], b[~nb])
+
+
+def test_mx_reduce_decodes_every_code_under_every_scale(zs):
+    """P = 1, inv_scale = 1: the reduce output is the decoded MXFP8 value of
+    all 256 codes under each of the 256 scale bytes (65536 pairs)."""
+    import torch
+    codes = np.tile(np.arange(256, dtype=np.uint8), 256)
+    scales = np.repeat(np.arange(256, dtype=np.uint8), 8)       # 8 blocks of 32 per byte
+    want = O.mxfp8_decode(codes, scales)
+    # NaN: every code under scale 0xFF, and codes 0x7F / 0xFF under the others
+    assert int(np.isnan(want).sum()) == 256 + 255 * 2
+    g = torch.empty(codes.size, dtype=torch.float32, device="cuda")
+    acc = zs.new_norm_acc(1)
+    zs.zero_shard_reduce_mx([to_dev(codes)], [to_dev(scales)], 1.0, g_out=g, acc=acc)
+    torch.cuda.synchronize()
+    got = from_dev(g)
+    bad = np.nonzero(~((got == want) | (np.isnan(got) & np.isnan(want))))[0]
+    assert bad.size == 0, [(int(codes[i]), int(scales[i // 32]), got[i], want[i]) for i in bad[:6]]
+    assert _same_or_both_nan(got, want)
+    assert zs.read_norm_acc(acc)[0] == acc_from_oracle(O.norm_accumulate(want))
+
+
+@pytest.mark.parametrize("P", [1, 3, 8])
+def test_mx_reduce_and_norm(zs, P):
+    """Replicas packed to MXFP8 by the oracle (with inf/NaN blocks, all-zero
+    blocks and tiny blocks) against decode-then-reduce in the oracle."""
+    import torch
+    for n in (32, 64, 32 * 33, 32 * 4099, 32 * 65537):
+        reps = _replicas(P, n, True, seed=n + P)
+        if n >= 1024:
+            reps[0][3] = 0x7FC0                  # NaN: its block's scale is NaN
+            reps[P - 1][n - 1] = 0x7F80          # +inf
+            reps[P // 2][64:96] = 0              # an all-zero block
+            reps[0][96:128] = O.f32_to_bf16(np.full(32, 1e-30, np.float32))
+        packed = [O.mxfp8_pack(r) for r in reps]
+        inv = O.inv_scale(P, 1.0)
+        want_g = O.reduce([O.mxfp8_decode(e, s) for e, s in packed], inv)
+        want_acc = acc_from_oracle(O.norm_accumulate(want_g))
+        codes = [to_dev(e) for e, _ in packed]
+        scales = [to_dev(s) for _, s in packed]
+        g = torch.empty(n, dtype=torch.float32, device="cuda")
+        acc = zs.new_norm_acc(1)
+        zs.zero_shard_reduce_mx(codes, scales, inv, g_out=g, acc=acc)
+        acc2 = zs.new_norm_acc(1)
+        zs.zero_shard_reduce_mx(codes, scales, inv, acc=acc2)
+        torch.cuda.synchronize()
+        got = from_dev(g)
+        assert _same_or_both_nan(got, want_g), mismatch_report(f"g n={n}", got, want_g)
+        assert zs.read_norm_acc(acc)[0] == want_acc, n
+        assert zs.read_norm_acc(acc2)[0] == want_acc, n
+
+
+def test_mx_reduce_rejects_bad_sizes(zs):
+    import torch
+    c = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(2, dtype=torch.uint8, device="cuda")
+    g = torch.empty(64, dtype=torch.float32, device="cuda")
+    with pytest.raises(zs.ZeroStepError):
+        zs.zero_shard_reduce_mx([c[:48]], [s], 1.0, g_out=g[:48])      # n % 32 != 0
+    with pytest.raises((ValueError, zs.ZeroStepError)):
+        zs.zero_shard_reduce_mx([c], [s[:1]], 1.0, g_out=g)            # too few scales
+    with pytest.raises((ValueError, zs.ZeroStepError)):
+        zs.zero_shard_reduce_mx([c], [s], 1.0, g_out=g[:32])           # short g_out
+
+
+def test_shard_step_with_mxfp8_gradients(zs):
+    """ShardStep over MXFP8-stored replicas, gated (clip + overflow check),
+    with one overflowing call: the oracle step on the decoded replicas."""
+    import torch
+    n, P = 32 * 40_009, 8
+    lr, b1, b2, eps, wd, max_norm = 1e-3, 0.9, 0.999, 1e-8, 0.01, 0.05
+    master = synth.fill(synth.make_spec(seed=5, cfg=56, stream=0, sigma=0.02), 0, n, False)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    param = O.f32_to_bf16(master)
+    st = zs.ShardStep(n, P, "mxfp8", lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd,
+                      max_norm=max_norm, check_overflow=True, bucket=32 * 10_000)
+    assert st.path == "materialize"
+    st.master.copy_(to_dev(master))
+    st.param.copy_(to_dev(param))
+    t = 0
+    for call in range(1, 5):
+        reps = _replicas(P, n, True, seed=31 * call)
+        if call == 2:
+            reps[5][n // 2] = 0xFF80             # -inf: this call is skipped
+        packed = [O.mxfp8_pack(r) for r in reps]
+        skipped, _ = O.step([O.mxfp8_decode(e, s) for e, s in packed], O.inv_scale(P, 1.0),
+                            max_norm, True, lr, b1, b2, eps, wd, t + 1, master, m, v, param)
+        t += 0 if skipped else 1
+        st.step([(to_dev(e), to_dev(s)) for e, s in packed])
+    assert st.applied_steps() == t == 3
+    torch.cuda.synchronize()
+    for name, got, want in (("master", st.master, master), ("m", st.m, m), ("v", st.v, v),
+                            ("param", st.param, param)):
+        hg = from_dev(got, name == "param")
+        assert same_bits(hg, want), mismatch_report(name, hg, want)
+
+
 # ------------------------------------------------------------------ gate --
 
 def _acc_words(X, nonfinite, overflow, rng):

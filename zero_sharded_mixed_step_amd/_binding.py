@@ -12,7 +12,7 @@ import torch
 
 from . import build as _build
 
-ZERO_F32, ZERO_BF16 = 0, 1
+ZERO_F32, ZERO_BF16, ZERO_MXFP8 = 0, 1, 2
 ZERO_MAX_REPLICAS = 64
 ACC_WORDS = 8          # one zero_norm_acc = 64 bytes = 8 int64 words
 
@@ -57,6 +57,8 @@ def lib():
         L.zero_adamw_step.argtypes = [C.POINTER(_AdamArgs), vp]
         L.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
         L.zero_mxfp8_pack.argtypes = [vp, sz, vp, vp, vp]
+        L.zero_shard_reduce_mx.argtypes = [vp, vp, i, sz, C.c_float, vp, vp, vp]
+        L.zero_shard_reduce_mx.restype = i
         L.zero_unfused_workspace_bytes.argtypes = [sz, i]
         L.zero_unfused_workspace_bytes.restype = sz
         L.zero_adamw_step_unfused.argtypes = [C.POINTER(_AdamArgs), vp, sz, vp]
@@ -187,6 +189,26 @@ def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
     _check(lib().zero_shard_reduce(_ptr_array(reps, "replica"), len(reps), _dtype_code(reps[0]),
                                    n, float(inv_scale), _dev_ptr(g_out, "g_out"), ap,
                                    _stream(stream)), "zero_shard_reduce")
+
+
+def zero_shard_reduce_mx(codes, scales, inv_scale: float, g_out=None, acc=None, n=None,
+                         stream=None) -> None:
+    """Shard reduce of MXFP8-stored replicas: codes[k] uint8[n] and scales[k]
+    uint8[n/32] per rank (n % 32 == 0)."""
+    codes, scales = list(codes), list(scales)
+    if not codes or len(codes) != len(scales):
+        raise ValueError("one code array and one scale array per replica")
+    n = codes[0].numel() if n is None else int(n)
+    for c, sc in zip(codes, scales):
+        _need(c, n, "codes", U8)
+        _need(sc, n // 32, "scales", U8)
+    _need(g_out, n, "g_out", F32)
+    ap, k = _acc_ptr(acc)
+    if k > 1:
+        raise ValueError("zero_shard_reduce_mx adds to one accumulator")
+    _check(lib().zero_shard_reduce_mx(_ptr_array(codes, "codes"), _ptr_array(scales, "scales"),
+                                      len(codes), n, float(inv_scale), _dev_ptr(g_out, "g_out"),
+                                      ap, _stream(stream)), "zero_shard_reduce_mx")
 
 
 def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:

@@ -110,6 +110,33 @@ int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, f
   }
 }
 
+int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scales, int P,
+                         size_t n, float inv_scale, float* g_out, zero_norm_acc* acc,
+                         void* stream) {
+  try {
+    if (codes == nullptr || scales == nullptr || P < 1 || P > ZERO_MAX_REPLICAS)
+      return ZERO_EINVAL;
+    for (int k = 0; k < P; ++k) {
+      if (codes[k] == nullptr || scales[k] == nullptr) return ZERO_EINVAL;
+      if (!aligned16(codes[k])) return ZERO_EALIGN;
+    }
+    if (g_out == nullptr && acc == nullptr) return ZERO_EINVAL;
+    if ((g_out && !aligned16(g_out)) || (acc && !aligned16(acc))) return ZERO_EALIGN;
+    if (n % 32 != 0 || (acc != nullptr && n >= (size_t(1) << 32))) return ZERO_ESIZE;
+    if (n == 0) return ZERO_OK;
+    const void* c[ZERO_MAX_REPLICAS];
+    const void* sc[ZERO_MAX_REPLICAS];
+    for (int k = 0; k < P; ++k) {
+      c[k] = codes[k];
+      sc[k] = scales[k];
+    }
+    return status_of(zs::launch_reduce(c, P, ZERO_MXFP8, n, inv_scale, g_out, acc,
+                                       as_stream(stream), sc));
+  } catch (...) {
+    return ZERO_EHIP;
+  }
+}
+
 int zero_grad_norm(const void* grad, int dtype, size_t n, float inv_scale, zero_norm_acc* acc,
                    void* stream) {
   try {

@@ -20,8 +20,29 @@ constexpr int kThreads = 256;  // four wave64 wavefronts per workgroup
 constexpr int kVec = 8;        // elements per chunk
 
 struct Replicas {
-  const void* p[ZERO_MAX_REPLICAS];
+  const void* p[ZERO_MAX_REPLICAS];  // element data (MXFP8: the E4M3 codes)
+  const void* s[ZERO_MAX_REPLICAS];  // MXFP8 only: the scale bytes
 };
+
+// Eight MXFP8 elements (codes in lo/hi, block scale byte sb) decoded to
+// binary32: v_cvt_pk_f32_fp8 gives the exact E4M3 value, and the product
+// with the power of two 2^(sb - 127) is exact too (at least 2^-136, at most
+// 448 * 2^127 before rounding of an overflow to inf); sb == 0xFF is NaN.
+__device__ __forceinline__ void decode_mx8(uint32_t lo, uint32_t hi, uint32_t sb,
+                                           float x[8]) {
+  const float f = sb == 0xFFu ? __uint_as_float(0x7FC00000u)
+                  : (sb == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23));
+  const uint32_t w[2] = {lo, hi};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[h]), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[h]), true);
+    x[4 * h + 0] = a[0] * f;
+    x[4 * h + 1] = a[1] * f;
+    x[4 * h + 2] = b[0] * f;
+    x[4 * h + 3] = b[1] * f;
+  }
+}
 
 // ------------------------------------------------------------- loads ------
 
@@ -110,13 +131,26 @@ __device__ __forceinline__ void store_f32_chunk(float* base, uint64_t c, bool fu
 // g = (r_0 + r_1 + ... + r_{P-1}) * inv_scale in binary32, rank order.
 // PT > 0 fixes P at compile time (all P loads issue before the adds);
 // PT == 0 reads the runtime count.  Replicas are read once: NT loads.
+template <int DT>
+__device__ __forceinline__ void load_replica(const Replicas& R, int k, uint64_t c, bool full,
+                                             uint64_t n, float x[kVec]) {
+  if constexpr (DT == ZERO_MXFP8) {  // n % 32 == 0: chunks are always whole
+    const u32x2 w = load_stream<true>(
+        reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(R.p[k]) + c * kVec));
+    const uint32_t sb = static_cast<const uint8_t*>(R.s[k])[c >> 2];
+    decode_mx8(w.x, w.y, sb, x);
+  } else {
+    load_chunk<DT, true>(R.p[k], c, full, n, x);
+  }
+}
+
 template <int DT, int PT>
 __device__ __forceinline__ void reduce_chunk(const Replicas& R, int P, uint64_t c, bool full,
                                              uint64_t n, float inv_scale, float g[kVec]) {
   if constexpr (PT > 0) {
     float x[PT][kVec];
 #pragma unroll
-    for (int k = 0; k < PT; ++k) load_chunk<DT, true>(R.p[k], c, full, n, x[k]);
+    for (int k = 0; k < PT; ++k) load_replica<DT>(R, k, c, full, n, x[k]);
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       float s = x[0][j];
@@ -126,10 +160,10 @@ __device__ __forceinline__ void reduce_chunk(const Replicas& R, int P, uint64_t 
     }
   } else {
     float s[kVec];
-    load_chunk<DT, true>(R.p[0], c, full, n, s);
+    load_replica<DT>(R, 0, c, full, n, s);
     for (int k = 1; k < P; ++k) {
       float x[kVec];
-      load_chunk<DT, true>(R.p[k], c, full, n, x);
+      load_replica<DT>(R, k, c, full, n, x);
 #pragma unroll
       for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[j];
     }
@@ -143,7 +177,8 @@ __device__ __forceinline__ void reduce_chunk(const Replicas& R, int P, uint64_t 
 // of several chunks before any of them is summed.
 template <int DT, int PT>
 struct RawChunk {
-  static constexpr int kWords = DT == ZERO_BF16 ? 1 : 2;  // 16-byte vectors per replica
+  // 16-byte vectors per replica (MXFP8: codes in .x/.y, scale byte in .z)
+  static constexpr int kWords = DT == ZERO_F32 ? 2 : 1;
   u32x4 w[PT][kWords];
 };
 
@@ -154,6 +189,10 @@ __device__ __forceinline__ void load_raw(const Replicas& R, uint64_t c, RawChunk
     if constexpr (DT == ZERO_BF16) {
       r.w[k][0] = load_stream<true>(
           reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(R.p[k]) + c * kVec));
+    } else if constexpr (DT == ZERO_MXFP8) {
+      const u32x2 w = load_stream<true>(
+          reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(R.p[k]) + c * kVec));
+      r.w[k][0] = u32x4{w.x, w.y, static_cast<const uint8_t*>(R.s[k])[c >> 2], 0u};
     } else {
       const u32x4* p =
           reinterpret_cast<const u32x4*>(static_cast<const float*>(R.p[k]) + c * kVec);
@@ -176,6 +215,8 @@ __device__ __forceinline__ void sum_raw(const RawChunk<DT, PT>& r, float inv_sca
         x[k][2 * j] = __uint_as_float(ws[j] << 16);
         x[k][2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
       }
+    } else if constexpr (DT == ZERO_MXFP8) {
+      decode_mx8(r.w[k][0].x, r.w[k][0].y, r.w[k][0].z, x[k]);
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {

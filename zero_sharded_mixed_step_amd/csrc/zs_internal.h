@@ -29,9 +29,10 @@ struct AdamScalars {
 
 int compute_units(int device);
 
+// dtype ZERO_MXFP8: replicas are the code arrays and mx_scales the scales.
 hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t n,
                          float inv_scale, float* g_out, zero_norm_acc* acc,
-                         hipStream_t stream);
+                         hipStream_t stream, const void* const* mx_scales = nullptr);
 
 struct AdamLaunch {
   const float* grad;

@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
   };
   // Chunks per lane per fast-path iteration: enough to keep about 16
   // 16-byte loads in flight per lane whatever P and the dtype are.
-  constexpr int kRawLoads = PT > 0 ? PT * (DT == ZERO_BF16 ? 1 : 2) : 8;
+  constexpr int kRawLoads = PT > 0 ? PT * (DT == ZERO_F32 ? 2 : 1) : 8;
   constexpr int U = ZS_REDUCE_LOADS / kRawLoads < 1 ? 1
                     : (ZS_REDUCE_LOADS / kRawLoads > 8 ? 8 : ZS_REDUCE_LOADS / kRawLoads);
   const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
@@ -204,9 +204,11 @@ static void reduce_dispatch_p(const ReduceParams& prm, bool write, bool norm, un
 
 hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t n,
                          float inv_scale, float* g_out, zero_norm_acc* acc,
-                         hipStream_t stream) {
+                         hipStream_t stream, const void* const* mx_scales) {
   ReduceParams prm;
   prm.R = pack_replicas(replicas, P);
+  if (mx_scales != nullptr)
+    for (int k = 0; k < P; ++k) prm.R.s[k] = mx_scales[k];
   prm.P = P;
   prm.inv_scale = inv_scale;
   prm.n = n;
@@ -214,10 +216,13 @@ hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t
   prm.g_out = g_out;
   prm.acc = acc;
   const unsigned grid = grid_for(prm.nchunks, ZS_REDUCE_BLOCKS_PER_CU);
+  const bool write = g_out != nullptr, norm = acc != nullptr;
   if (dtype == ZERO_BF16)
-    reduce_dispatch_p<ZERO_BF16>(prm, g_out != nullptr, acc != nullptr, grid, stream);
+    reduce_dispatch_p<ZERO_BF16>(prm, write, norm, grid, stream);
+  else if (dtype == ZERO_MXFP8)
+    reduce_dispatch_p<ZERO_MXFP8>(prm, write, norm, grid, stream);
   else
-    reduce_dispatch_p<ZERO_F32>(prm, g_out != nullptr, acc != nullptr, grid, stream);
+    reduce_dispatch_p<ZERO_F32>(prm, write, norm, grid, stream);
   return hipGetLastError();
 }
 

@@ -47,7 +47,17 @@ class ShardStep:
         self.bucket = int(bucket) if bucket else None
         if self.bucket is not None and self.bucket % 32:
             raise ValueError("buckets must be multiples of 32 elements")
+        # grad_dtype: torch.float32, torch.bfloat16, or "mxfp8" (replicas given
+        # as (codes, scales) pairs; only the reduce pass reads them, so the
+        # gradient is always materialised)
+        self.mx_grads = grad_dtype == "mxfp8"
         g_b = 4 if grad_dtype == torch.float32 else 2
+        if self.mx_grads:
+            if path not in (None, "materialize"):
+                raise ValueError("MXFP8 gradient replicas need the materialise path")
+            if self.n % 32:
+                raise ValueError("MXFP8 gradients need n % 32 == 0")
+            path = "materialize"
         if path is None:
             if not self.gated:
                 path = "fused"
@@ -104,6 +114,12 @@ class ShardStep:
         if self.path == "fused":
             return
         for lo, hi in self._ranges():
+            if self.mx_grads:
+                codes = [c[lo:hi] for c, _ in replicas]
+                scales = [sc[lo // 32:hi // 32] for _, sc in replicas]
+                B.zero_shard_reduce_mx(codes, scales, self.inv_scale, g_out=self.g[lo:hi],
+                                       acc=self.acc)
+                continue
             views = [r[lo:hi] for r in replicas]
             if self.path == "materialize":
                 B.zero_shard_reduce(views, self.inv_scale, g_out=self.g[lo:hi], acc=self.acc)
