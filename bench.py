@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements of the CPU-oracle sample")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the offload bill (PCIe copies + all-cores CPU AdamW)")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="threads of the all-cores oracle legs (capped by the host)")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused single-operation chain")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -172,9 +176,11 @@ def copy_calibration():
           flush=True)
 
 
-def cpu_baseline(w, sample, steps):
-    """The CPU oracle, untuned and single-threaded, on the first `sample`
-    elements of the workload's shard (inputs generated beforehand)."""
+def cpu_baseline(w, sample, steps, threads=1):
+    """The CPU oracle on the first `sample` elements of the workload's shard
+    (inputs generated beforehand): single-threaded as it stands, or with
+    threads > 1 its threaded driver (32-aligned slices, bitwise the same
+    result)."""
     import numpy as np
 
     import oracle as O
@@ -193,22 +199,127 @@ def cpu_baseline(w, sample, steps):
         reps = [O.mxfp8_pack(r[:sample]) for r in reps]
         master, m, v, param, g_tmp = (a[:sample] for a in (master, m, v, param, g_tmp))
     inv = O.inv_scale(w.P, w.loss_scale)
-    elem = np.empty(sample, np.uint8) if w.pack else None
+    from concurrent.futures import ThreadPoolExecutor
+    ex = ThreadPoolExecutor(threads) if threads > 1 else None
+    psample = sample // 32 * 32
+    cuts = O._cuts(psample, threads)
+
+    def decode_all():
+        if ex is None:
+            return [O.mxfp8_decode(e, sc) for e, sc in reps]
+        out = [np.empty(sample, np.float32) for _ in reps]
+
+        def part(c):
+            for o, (e, sc) in zip(out, reps):
+                o[c[0]:c[1]] = O.mxfp8_decode(e[c[0]:c[1]], sc[c[0] // 32:c[1] // 32])
+        list(ex.map(part, cuts))
+        return out
+
+    def pack_param():
+        if ex is None:
+            return O.mxfp8_pack(param[:psample])
+        list(ex.map(lambda c: O.mxfp8_pack(param[c[0]:c[1]]), cuts))
+
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
         # MXFP8-stored replicas: the decode is part of the timed step
-        g_in = [O.mxfp8_decode(e, sc) for e, sc in reps] if w.mx_grads else reps
-        O.step(g_in, inv, w.max_norm, w.check_overflow, w.lr, w.beta1, w.beta2, w.eps,
-               w.wd, t, master, m, v, param, g_tmp=g_tmp)
+        g_in = decode_all() if w.mx_grads else reps
+        if ex is not None:
+            O.step_parallel(g_in, inv, w.max_norm, w.check_overflow, w.lr, w.beta1, w.beta2,
+                            w.eps, w.wd, t, master, m, v, param, g_tmp=g_tmp, threads=threads)
+        else:
+            O.step(g_in, inv, w.max_norm, w.check_overflow, w.lr, w.beta1, w.beta2, w.eps,
+                   w.wd, t, master, m, v, param, g_tmp=g_tmp)
         if w.pack:
-            elem, _ = O.mxfp8_pack(param[: sample // 32 * 32])
+            pack_param()
     dt = time.perf_counter() - t0
+    if ex is not None:
+        ex.shutdown()
     rate = sample * steps / dt
-    return {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+    return {"value": rate, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"first {sample} elements of the {w.name} shard, {steps} steps, "
-                      f"inputs pre-generated, single thread",
+                      f"inputs pre-generated, "
+                      + ("single thread" if threads == 1 else f"{threads} threads"),
             "seconds": round(dt, 3), "cpu": platform.processor() or platform.machine(),
             "host_cpus": os.cpu_count()}
+
+
+def offload_bill(w, threads, sample, gpu_step_ms, reduce_ms):
+    """What the step costs with the optimizer moved to the host (the
+    offloading the ZeRO pages describe): the GPU still reduces (its measured
+    reduce time), the fp32 averaged gradient shard crosses PCIe to pinned
+    host memory, the CPU runs the gate + AdamW on all its cores (the
+    oracle's AdamW, threaded over slices: the same arithmetic, so the same
+    bits), and the bf16 param shard crosses back.  Transfer rates and the
+    CPU rate are measured on bounded samples and scaled to the shard."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    import synth
+    dev = torch.device("cuda:0")
+    nt = 1 << 28                                    # 1 GiB of fp32, 512 MiB of bf16
+    g_dev = torch.empty(nt, dtype=torch.float32, device=dev)
+    p_dev = torch.empty(nt, dtype=torch.int16, device=dev)
+    g_host = torch.empty(nt, dtype=torch.float32, pin_memory=True)
+    p_host = torch.zeros(nt, dtype=torch.int16, pin_memory=True)
+    g_dev.fill_(1.0)
+
+    def copy_rate(dst, src, nbytes, reps=3):
+        dst.copy_(src, non_blocking=True)           # warm
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        return nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+    d2h = copy_rate(g_host, g_dev, 4 * nt)
+    h2d = copy_rate(p_dev, p_host, 2 * nt)
+    del g_dev, p_dev, g_host, p_host
+
+    sample = min(sample, w.S) // 32 * 32
+    start = w.shard_start()
+    master = synth.fill(w.master_spec(), start, sample, False, threads=8)
+    m, v = np.zeros(sample, np.float32), np.zeros(sample, np.float32)
+    param = np.zeros(sample, np.uint16)
+    reps = [synth.fill(w.grad_spec(1, k), start, sample, w.grad_bf16, threads=8)
+            for k in range(w.P)]
+    g = O.reduce(reps, O.inv_scale(w.P, w.loss_scale))
+    del reps
+    cuts = O._cuts(sample, threads)
+    from concurrent.futures import ThreadPoolExecutor
+    reps_t = 3
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        for t in range(1, reps_t + 1):
+            s = O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, t)
+            list(ex.map(lambda c: O.adamw(g[c[0]:c[1]], 0.5, s, master[c[0]:c[1]],
+                                          m[c[0]:c[1]], v[c[0]:c[1]], param[c[0]:c[1]]),
+                        cuts))
+        dt = time.perf_counter() - t0
+    cpu_rate = sample * reps_t / dt
+    S = w.S
+    d2h_ms = 4 * S / (d2h * 1e9) * 1e3
+    cpu_ms = S / cpu_rate * 1e3
+    h2d_ms = 2 * S / (h2d * 1e9) * 1e3
+    serial = reduce_ms + d2h_ms + cpu_ms + h2d_ms
+    pipelined = reduce_ms + max(d2h_ms, cpu_ms, h2d_ms)
+    return {"d2h_gbps": round(d2h, 1), "h2d_gbps": round(h2d, 1),
+            "cpu_adamw_params_per_s": round(cpu_rate, 1), "cpu_threads": threads,
+            "per_step_ms": {"gpu_reduce": round(reduce_ms, 3), "d2h_g_f32": round(d2h_ms, 2),
+                            "cpu_adamw": round(cpu_ms, 2), "h2d_param_bf16": round(h2d_ms, 2)},
+            "offloaded_ms_per_step_serial": round(serial, 2),
+            "offloaded_ms_per_step_pipelined": round(pipelined, 2),
+            "gpu_ms_per_step": round(gpu_step_ms, 3),
+            "slowdown_serial": round(serial / gpu_step_ms, 1),
+            "slowdown_pipelined": round(pipelined / gpu_step_ms, 1),
+            "sample": f"PCIe: 1 GiB D2H fp32 and 512 MiB H2D bf16, pinned, x3; CPU: oracle "
+                      f"AdamW on the first {sample} elements of the {w.name} shard x{reps_t}; "
+                      f"scaled to S={S}"}
 
 
 def main():
@@ -275,10 +386,20 @@ def main():
         b.record()
         events[kind].append((a, b))
 
+    step_events = []
+
     def one_step(record):
         if not record:
             st.step(reps)
             return
+        sa = torch.cuda.Event(enable_timing=True)
+        sb = torch.cuda.Event(enable_timing=True)
+        sa.record()
+        _launch_step()
+        sb.record()
+        step_events.append((sa, sb))
+
+    def _launch_step():
         if st.path == "fused":
             zs.zero_norm_acc_clear(st.acc)
         else:
@@ -338,6 +459,8 @@ def main():
     params_per_s = w.S / (elapsed / args.steps)
     gbps = step_bytes / (elapsed / args.steps) / 1e9
     kernel_ms = {k: sum(a.elapsed_time(b) for a, b in ev) / len(ev) for k, ev in events.items()}
+    step_ms = sorted(a.elapsed_time(b) for a, b in step_events)
+    p90 = step_ms[min(len(step_ms) - 1, int(round(0.9 * (len(step_ms) - 1))))]
     per_kernel = {k: {"avg_ms": round(kernel_ms[k], 4),
                       "bytes_per_elem": kinds[k],
                       "gbps": round(kinds[k] * w.S / (kernel_ms[k] * 1e-3) / 1e9, 1)}
@@ -360,6 +483,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_median": round(statistics.median(step_ms), 4),
+        "step_ms_p90": round(p90, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -386,9 +511,17 @@ def main():
                                      "scaled by a plain-copy calibration)",
                      "traffic_vs_algorithmic": traffic[1] if traffic else None},
         "cpu_baseline": None,
+        "cpu_baseline_all_cores": None,
+        "offload_bill": None,
     }
+    threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+    if not args.no_offload and "reduce" in kernel_ms:
+        out["offload_bill"] = offload_bill(w, threads, args.cpu_sample, ms_per_step,
+                                           kernel_ms["reduce"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps)
+        out["cpu_baseline_all_cores"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps,
+                                                     threads=threads)
     print(json.dumps(out), flush=True)
 
 

@@ -230,6 +230,49 @@ def step(replicas, inv_scale_f, max_norm, check_overflow, lr, beta1, beta2, eps,
     return bool(rc), own
 
 
+def _cuts(n: int, parts: int):
+    per = max(32, ((n + parts - 1) // parts + 31) // 32 * 32)
+    return [(a, min(n, a + per)) for a in range(0, n, per)]
+
+
+def step_parallel(replicas, inv_scale_f, max_norm, check_overflow, lr, beta1, beta2, eps,
+                  wd, t, master, m, v, param=None, g_tmp=None, threads=None):
+    """The same step as `step`, spread over threads (the ctypes calls release
+    the GIL): reduce + norm state per 32-aligned slice, the integer norm
+    states added, then AdamW per slice.  Integer addition is associative, so
+    the result is bit for bit that of `step`.  Returns (skipped, own_acc)."""
+    from concurrent.futures import ThreadPoolExecutor
+    reps = [np.ascontiguousarray(r) for r in replicas]
+    n = reps[0].size
+    threads = threads or os.cpu_count() or 1
+    if g_tmp is None:
+        g_tmp = np.empty(n, dtype=np.float32)
+    cuts = _cuts(n, threads)
+
+    def first(c):
+        a, b = c
+        g_tmp[a:b] = reduce([r[a:b] for r in reps], inv_scale_f)
+        return norm_accumulate(g_tmp[a:b])
+
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(first, cuts))
+        own = acc_zero()
+        for part in parts:
+            acc_add(own, part)
+        if check_overflow and (own.nonfinite + own.overflow) > 0:
+            return True, own
+        coef = clip_coef(acc_sumsq(own), max_norm)
+        s = make_scalars(lr, beta1, beta2, eps, wd, t)
+
+        def second(c):
+            a, b = c
+            adamw(g_tmp[a:b], coef, s, master[a:b], m[a:b], v[a:b],
+                  None if param is None else param[a:b])
+
+        list(ex.map(second, cuts))
+    return False, own
+
+
 # ----------------------------------------------------------------- MXFP8 ---
 
 def e4m3_encode(q: float) -> int:
