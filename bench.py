@@ -49,7 +49,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="C5", choices=["C1", "C2", "C3", "C4", "C5", "C5M"])
+    ap.add_argument("--config", default="30b-shard-p8",
+                    choices=["flat-1m-p4", "gpt2-small-p8", "1.3b-unsharded", "7b-shard-p8",
+                             "30b-shard-p8", "30b-shard-p8-mxgrads"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements of the CPU-oracle sample")
@@ -322,6 +324,18 @@ def offload_bill(w, threads, sample, gpu_step_ms, reduce_ms):
                       f"scaled to S={S}"}
 
 
+def cpu_baseline_leg(w, args, threads, gpu_step_ms, reduce_ms):
+    """The host side of the report, all of it the CPU oracle: single-threaded
+    on a bounded sample (the baseline proper), the same on all cores, and the
+    offload bill (the GPU reduce's measured time + PCIe + the oracle's AdamW
+    on all cores) that moving the optimizer to the host would cost."""
+    res = cpu_baseline(w, args.cpu_sample, args.cpu_steps)
+    res["all_cores"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps, threads=threads)
+    if not args.no_offload and reduce_ms is not None:
+        res["offload_bill"] = offload_bill(w, threads, args.cpu_sample, gpu_step_ms, reduce_ms)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -511,17 +525,11 @@ def main():
                                      "scaled by a plain-copy calibration)",
                      "traffic_vs_algorithmic": traffic[1] if traffic else None},
         "cpu_baseline": None,
-        "cpu_baseline_all_cores": None,
-        "offload_bill": None,
     }
     threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
-    if not args.no_offload and "reduce" in kernel_ms:
-        out["offload_bill"] = offload_bill(w, threads, args.cpu_sample, ms_per_step,
-                                           kernel_ms["reduce"])
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps)
-        out["cpu_baseline_all_cores"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps,
-                                                     threads=threads)
+        out["cpu_baseline"] = cpu_baseline_leg(w, args, threads, ms_per_step,
+                                               kernel_ms.get("reduce"))
     print(json.dumps(out), flush=True)
 
 

@@ -71,32 +71,39 @@ class Workload:
         return r * self.S
 
 
-C1 = Workload("C1", "flat N=1,048,576, P=4 fp32 replicas, rank-0 shard, 1 step",
-              N=1_048_576, P=4, S=262_144, grad_bf16=False, grad_sigma=1e-2, steps=1,
-              cfg_id=1)
-C2 = Workload("C2", "GPT-2-small-sized N=124,439,808, P=8 bf16 replicas with 1% x100 "
-              "outliers, shard N/8, 10 steps, clip 1.0",
-              N=124_439_808, P=8, S=15_554_976, grad_bf16=True, grad_sigma=1e-3,
-              steps=10, max_norm=1.0, outlier_rate=0.01, cfg_id=2)
-C3 = Workload("C3", "1.3B unsharded P=1, bf16 grads x65536 loss scale, 10 calls, "
-              "overflow check with one injected inf",
-              N=1_300_000_000, P=1, S=1_300_000_000, grad_bf16=True, grad_sigma=1e-3,
-              steps=10, check_overflow=True, loss_scale=65536.0,
-              inject=(5, 1_300_000_000 // 3), cfg_id=3)
-C4 = Workload("C4", "7B model, rank-0 shard of 875M at P=8, 8 bf16 replicas in 25M "
-              "buckets, 10 steps, clip 1.0",
-              N=7_000_000_000, P=8, S=875_000_000, grad_bf16=True, grad_sigma=1e-3,
-              steps=10, max_norm=1.0, bucket=25_000_000, cfg_id=4)
-C5 = Workload("C5", "30B model ZeRO-3, rank-0 shard of 3.75B at P=8, 8 bf16 replicas, "
-              "clip 1.0 + overflow check, 5 steps, then MXFP8 pack",
-              N=30_000_000_000, P=8, S=3_750_000_000, grad_bf16=True, grad_sigma=1e-3,
-              steps=5, max_norm=1.0, check_overflow=True, pack=True, cfg_id=5)
+FLAT_1M = Workload(
+    "flat-1m-p4", "flat N=1,048,576, P=4 fp32 replicas, rank-0 shard, 1 step",
+    N=1_048_576, P=4, S=262_144, grad_bf16=False, grad_sigma=1e-2, steps=1, cfg_id=1)
+GPT2_SMALL = Workload(
+    "gpt2-small-p8", "GPT-2-small-sized N=124,439,808, P=8 bf16 replicas with 1% x100 "
+    "outliers, shard N/8, 10 steps, clip 1.0",
+    N=124_439_808, P=8, S=15_554_976, grad_bf16=True, grad_sigma=1e-3,
+    steps=10, max_norm=1.0, outlier_rate=0.01, cfg_id=2)
+UNSHARDED_1P3B = Workload(
+    "1.3b-unsharded", "1.3B unsharded P=1, bf16 grads x65536 loss scale, 10 calls, "
+    "overflow check with one injected inf",
+    N=1_300_000_000, P=1, S=1_300_000_000, grad_bf16=True, grad_sigma=1e-3,
+    steps=10, check_overflow=True, loss_scale=65536.0,
+    inject=(5, 1_300_000_000 // 3), cfg_id=3)
+SHARD_7B = Workload(
+    "7b-shard-p8", "7B model, rank-0 shard of 875M at P=8, 8 bf16 replicas in 25M "
+    "buckets, 10 steps, clip 1.0",
+    N=7_000_000_000, P=8, S=875_000_000, grad_bf16=True, grad_sigma=1e-3,
+    steps=10, max_norm=1.0, bucket=25_000_000, cfg_id=4)
+SHARD_30B = Workload(
+    "30b-shard-p8", "30B model ZeRO-3, rank-0 shard of 3.75B at P=8, 8 bf16 replicas, "
+    "clip 1.0 + overflow check, 5 steps, then MXFP8 pack",
+    N=30_000_000_000, P=8, S=3_750_000_000, grad_bf16=True, grad_sigma=1e-3,
+    steps=5, max_norm=1.0, check_overflow=True, pack=True, cfg_id=5)
 
-# The 30B shard with its gradient replicas stored as MXFP8 (the bf16
-# replicas of C5, packed), the stored-state saving of the pages' MXFP8 item.
-C5M = Workload("C5M", "30B model ZeRO-3, rank-0 shard of 3.75B at P=8, 8 MXFP8-stored grad "
-               "replicas, clip 1.0 + overflow check, 5 steps, MXFP8 param pack",
-               N=30_000_000_000, P=8, S=3_750_000_000, grad_bf16=True, grad_sigma=1e-3,
-               steps=5, max_norm=1.0, check_overflow=True, pack=True, mx_grads=True, cfg_id=5)
+# The 30B shard with its gradient replicas stored as MXFP8 (the bf16 replicas
+# of the 30B shard above, packed): the stored-state saving of the pages' MXFP8
+# item.
+SHARD_30B_MX = Workload(
+    "30b-shard-p8-mxgrads", "30B model ZeRO-3, rank-0 shard of 3.75B at P=8, 8 MXFP8-stored "
+    "grad replicas, clip 1.0 + overflow check, 5 steps, MXFP8 param pack",
+    N=30_000_000_000, P=8, S=3_750_000_000, grad_bf16=True, grad_sigma=1e-3,
+    steps=5, max_norm=1.0, check_overflow=True, pack=True, mx_grads=True, cfg_id=5)
 
-ALL = {w.name: w for w in (C1, C2, C3, C4, C5, C5M)}
+ALL = {w.name: w for w in (FLAT_1M, GPT2_SMALL, UNSHARDED_1P3B, SHARD_7B, SHARD_30B,
+                            SHARD_30B_MX)}

@@ -93,7 +93,7 @@ def _compare_state(st, want, where=""):
 
 def test_flat_1m_p4_fp32_all_ranks(zs):
     import torch
-    w = configs.C1
+    w = configs.FLAT_1M
     for rank in range(w.P):
         lo = rank * w.S
         st = _step_for(zs, w)
@@ -115,7 +115,7 @@ def test_flat_1m_p4_fp32_all_ranks(zs):
 @pytest.mark.timeout(900)
 def test_gpt2_small_p8_ten_steps_all_ranks(zs):
     import torch
-    w = configs.C2
+    w = configs.GPT2_SMALL
     ranks = [_step_for(zs, w) for _ in range(w.P)]
     for r, st in enumerate(ranks):
         _init_state(st, w, r * w.S)
@@ -232,7 +232,7 @@ def _run_sampled(zs, w, calls, seed):
 def test_1p3b_unsharded_loss_scale_skip(zs):
     # calls 1..6 of 10: covers the injected overflow at call 5 and the
     # applied step after it
-    w = configs.C3
+    w = configs.UNSHARDED_1P3B
     st, _, gates = _run_sampled(zs, w, calls=range(1, 7), seed=3)
     assert [s for _, s in gates] == [False, False, False, False, True, False]
     assert st.path == "recompute"
@@ -242,7 +242,7 @@ def test_1p3b_unsharded_loss_scale_skip(zs):
 @pytest.mark.timeout(900)
 def test_7b_shard_35_buckets_clip(zs):
     # 2 of the 10 steps at the full 875M shard, 35 buckets of 25M
-    w = configs.C4
+    w = configs.SHARD_7B
     st, _, _ = _run_sampled(zs, w, calls=range(1, 3), seed=4)
     assert st.path == "materialize" and st.bucket == 25_000_000
 
@@ -251,7 +251,7 @@ def test_7b_shard_35_buckets_clip(zs):
 def test_30b_shard_clip_overflow_then_mxfp8(zs):
     # 2 of the 5 steps at the full 3.75B shard, then the MXFP8 pack
     import torch
-    w = configs.C5
+    w = configs.SHARD_30B
     rng = np.random.default_rng(5)
     st, idx, gates = _run_sampled(zs, w, calls=range(1, 3), seed=5)
     blocks = np.unique(rng.integers(0, w.S // 32, size=256))
@@ -276,7 +276,7 @@ def test_30b_shard_mxfp8_stored_grads(zs):
     # 1 of the 5 steps at the full 3.75B shard: the host oracle packs and
     # decodes all 8 replicas of the whole shard for the norm (~2 min on 16
     # threads), so one call is what fits
-    w = configs.C5M
+    w = configs.SHARD_30B_MX
     st, idx, gates = _run_sampled(zs, w, calls=range(1, 2), seed=6)
     assert st.path == "materialize" and idx.size % 32 == 0
     assert gates[0][1] is False

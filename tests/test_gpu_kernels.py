@@ -584,3 +584,49 @@ def test_runs_are_bitwise_reproducible(zs):
         outs.append([t.cpu().numpy().copy() for t in (st.master, st.m, st.v, st.param, st.acc)])
     for a, b in zip(*outs):
         assert same_bits(a, b)
+
+
+# ------------------------------------------------------ zero-length calls --
+
+def test_zero_length_calls_touch_nothing(zs):
+    """n = 0 is a valid no-op for every entry point: status ok, no element of
+    any output written.  AdamW still reports its gate decision through
+    skipped_out (a rank whose shard slice is empty takes part in the step)."""
+    import torch
+    n = 64
+    reps = [to_dev(r) for r in _replicas(2, n, True, seed=5, inject=[(1, 9, np.inf)])]
+    g = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    acc = zs.new_norm_acc(1)
+    zs.zero_shard_reduce(reps, 0.5, g_out=g, acc=acc, n=0)
+    zs.zero_grad_norm(reps[0], 0.5, acc, n=0)
+    codes = [torch.zeros(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    scales = [torch.zeros(n // 32, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    zs.zero_shard_reduce_mx(codes, scales, 0.5, g_out=g, acc=acc, n=0)
+    elem = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    scale = torch.full((n // 32,), 0xCD, dtype=torch.uint8, device="cuda")
+    zs.zero_mxfp8_pack(reps[0], elem, scale, n=0)
+    torch.cuda.synchronize()
+    assert torch.all(g == 7.0).item()
+    assert zs.read_norm_acc(acc)[0] == (0, 0, 0)
+    assert torch.all(elem == 0xAB).item() and torch.all(scale == 0xCD).item()
+
+    bad = zs.new_norm_acc(1)
+    zs.zero_shard_reduce(reps, 0.5, acc=bad)            # one inf -> nonfinite 1
+    master = torch.full((n,), 0.25, dtype=torch.float32, device="cuda")
+    m = torch.full((n,), 0.5, dtype=torch.float32, device="cuda")
+    v = torch.full((n,), 0.75, dtype=torch.float32, device="cuda")
+    param = torch.full((n,), 0x1234, dtype=torch.int16, device="cuda")
+    skipped = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    for accs, check, want_skip in ((bad, True, 1), (acc, True, 0), (bad, False, 0)):
+        skipped.fill_(-5)
+        zs.zero_adamw_step(master, m, v, step=1, lr=1e-3, weight_decay=0.01, grad_f32=g,
+                           param_bf16=param, accs=accs, max_norm=1.0, check_overflow=check,
+                           skipped_out=skipped, mx_elem_out=elem, mx_scale_out=scale, n=0)
+        zs.zero_adamw_step(master, m, v, step=1, lr=1e-3, replicas=reps, inv_scale=0.5,
+                           param_bf16=param, n=0)
+        torch.cuda.synchronize()
+        assert int(skipped.item()) == want_skip, (check, want_skip)
+    assert torch.all(master == 0.25).item() and torch.all(m == 0.5).item()
+    assert torch.all(v == 0.75).item() and torch.all(param == 0x1234).item()
+    assert torch.all(elem == 0xAB).item() and torch.all(scale == 0xCD).item()
+    assert torch.all(g == 7.0).item()

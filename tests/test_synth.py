@@ -39,7 +39,7 @@ def test_distribution():
 
 def test_streams_independent():
     n = 1 << 16
-    w = configs.C2
+    w = configs.GPT2_SMALL
     a = synth.fill(w.grad_spec(1, 0), 0, n, bf16=False).astype(np.float64)
     b = synth.fill(w.grad_spec(1, 1), 0, n, bf16=False).astype(np.float64)
     c = synth.fill(w.grad_spec(2, 0), 0, n, bf16=False).astype(np.float64)
@@ -59,5 +59,5 @@ def test_workload_table():
         assert w.S % 32 == 0 and w.N % w.S == 0 and w.N // w.S in (1, w.P)
         if w.bucket:
             assert w.S % w.bucket == 0 and w.bucket % 32 == 0
-    assert configs.C2.N == 8 * configs.C2.S
-    assert configs.C4.S // configs.C4.bucket == 35
+    assert configs.GPT2_SMALL.N == 8 * configs.GPT2_SMALL.S
+    assert configs.SHARD_7B.S // configs.SHARD_7B.bucket == 35
