@@ -115,6 +115,29 @@ def test_buckets_and_grid_shapes_do_not_change_the_norm(zs):
         assert zs.read_norm_acc(acc) == zs.read_norm_acc(whole), bucket
 
 
+@pytest.mark.parametrize("P,bf16", [(4, True), (8, True), (4, False), (8, False)])
+def test_pipelined_reduce_many_iterations(zs, P, bf16):
+    """With 4 or 8 replicas the reduce's fast path is software pipelined over
+    a one-workgroup-per-CU grid: sizes of a few million elements run many
+    pipeline stages per workgroup, then a ragged tail (not a multiple of 8)."""
+    import torch
+    n = 3 * (1 << 20) + 8 * 1000 + 5
+    reps = _replicas(P, n, bf16, seed=11, inject=[(P - 1, n // 2, np.inf)])
+    inv = O.inv_scale(P, 1.0)
+    want_g = O.reduce(reps, inv)
+    want_acc = acc_from_oracle(O.norm_accumulate(want_g))
+    dreps = [to_dev(r) for r in reps]
+    g = torch.empty(n, dtype=torch.float32, device="cuda")
+    acc = zs.new_norm_acc(1)
+    zs.zero_shard_reduce(dreps, inv, g_out=g, acc=acc)
+    acc2 = zs.new_norm_acc(1)
+    zs.zero_shard_reduce(dreps, inv, acc=acc2)
+    torch.cuda.synchronize()
+    assert same_bits(from_dev(g), want_g), mismatch_report("g", from_dev(g), want_g)
+    assert zs.read_norm_acc(acc)[0] == want_acc
+    assert zs.read_norm_acc(acc2)[0] == want_acc
+
+
 # ------------------------------------------------- MXFP8-stored replicas --
 
 def _same_or_both_nan(a: np.ndarray, b: np.ndarray) -> bool:

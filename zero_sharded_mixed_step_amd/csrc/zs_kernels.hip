@@ -5,6 +5,8 @@
 // workgroups per compute unit striding over 2048-element tiles, and the norm
 // state reduced in registers (quad DPP), lane-private LDS rows and one set
 // of integer atomics per workgroup.
+#include <atomic>
+
 #include "zs_device.h"
 #include "zs_internal.h"
 
@@ -35,6 +37,42 @@ static unsigned grid_for(uint64_t nchunks, int blocks_per_cu) {
   return static_cast<unsigned>(g > 0 ? g : 1);
 }
 
+// Workgroups of `kernel` that one compute unit holds at once (set by its
+// register and LDS footprint), from the runtime's occupancy query, cached per
+// kernel; `fallback` if the runtime cannot tell.  A persistent grid of exactly
+// this many workgroups per CU runs in one round: a larger one would run as a
+// full round followed by a partial one.
+static int resident_per_cu(const void* kernel, int fallback) {
+  constexpr int kSlots = 64;
+  static std::atomic<const void*> keys[kSlots];
+  static std::atomic<int> vals[kSlots];
+  int slot = -1;
+  for (int i = 0; i < kSlots; ++i) {
+    const void* k = keys[i].load(std::memory_order_acquire);
+    if (k == kernel) {
+      const int v = vals[i].load(std::memory_order_relaxed);
+      if (v > 0) return v;
+      slot = i;
+      break;
+    }
+    if (k == nullptr) {
+      const void* expected = nullptr;
+      if (keys[i].compare_exchange_strong(expected, kernel) || expected == kernel) {
+        slot = i;
+        break;
+      }
+    }
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, 0) != hipSuccess ||
+      nb <= 0) {
+    (void)hipGetLastError();  // the query's own failure is not a launch error
+    nb = fallback;
+  }
+  if (slot >= 0) vals[slot].store(nb, std::memory_order_relaxed);
+  return nb;
+}
+
 static Replicas pack_replicas(const void* const* replicas, int P) {
   Replicas R{};
   for (int k = 0; k < P; ++k) R.p[k] = replicas[k];
@@ -56,10 +94,17 @@ struct ReduceParams {
 #ifndef ZS_REDUCE_LOADS
 #define ZS_REDUCE_LOADS 24
 #endif
+#ifndef ZS_REDUCE_PIPE_LOADS
+#define ZS_REDUCE_PIPE_LOADS 16
+#endif
+#ifndef ZS_REDUCE_PIPE_MAX_ELEMS
+#define ZS_REDUCE_PIPE_MAX_ELEMS (1ull << 27)
+#endif
 
 
-template <int DT, int PT, bool WRITE, bool NORM>
+template <int DT, int PT, bool WRITE, bool NORM, bool PIPE>
 __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm) {
+  static_assert(!PIPE || PT >= 4, "the pipelined fast path is built for 4 or 8 replicas");
   __shared__ uint64_t s_digit[NORM ? 7 : 1][kThreads];
   __shared__ uint32_t s_count[NORM ? 2 : 1][kThreads];
   const int tid = threadIdx.x;
@@ -97,37 +142,73 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
     fixed_point_piece(S, quad_lane, d, piece);
     if (piece != 0) s_digit[d][tid] += piece;  // lane-private row
   };
-  // Chunks per lane per fast-path iteration: enough to keep about 16
-  // 16-byte loads in flight per lane whatever P and the dtype are.
+  // Chunks per lane per fast-path iteration.  PIPE (4 or 8 replicas, launches
+  // of up to ZS_REDUCE_PIPE_MAX_ELEMS elements) software-pipelines the fast
+  // path: the loads of the next U tiles are in flight while the current U
+  // tiles are summed, stored and squared, about ZS_REDUCE_PIPE_LOADS 16-byte
+  // loads per stage, on one workgroup per compute unit.  Otherwise about
+  // ZS_REDUCE_LOADS loads are issued, then consumed.
+  constexpr bool kPipe = PIPE;
   constexpr int kRawLoads = PT > 0 ? PT * (DT == ZERO_F32 ? 2 : 1) : 8;
-  constexpr int U = ZS_REDUCE_LOADS / kRawLoads < 1 ? 1
-                    : (ZS_REDUCE_LOADS / kRawLoads > 8 ? 8 : ZS_REDUCE_LOADS / kRawLoads);
+  constexpr int kLoads = kPipe ? ZS_REDUCE_PIPE_LOADS : ZS_REDUCE_LOADS;
+  constexpr int U = kLoads / kRawLoads < 1 ? 1
+                    : (kLoads / kRawLoads > 8 ? 8 : kLoads / kRawLoads);
   const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
   const uint64_t full_tiles = prm.n / (static_cast<uint64_t>(kThreads) * kVec);
   const uint64_t step = static_cast<uint64_t>(gridDim.x) * U;
   uint64_t tile = static_cast<uint64_t>(blockIdx.x) * U;
-  // Fast path: U whole tiles, no bounds checks, all loads issued up front.
-  for (; tile + U <= full_tiles; tile += step) {
-    if constexpr (PT > 0) {
-      RawChunk<DT, PT> raw[U];
+  // Fast path: U whole tiles at a time, no bounds checks.
+  if constexpr (kPipe) {
+    RawChunk<DT, PT> cur[U];
+    if (tile + U <= full_tiles) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_raw<DT, PT>(prm.R, (tile + u) * kThreads + tid, raw[u]);
-      __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first wait
+      for (int u = 0; u < U; ++u) load_raw<DT, PT>(prm.R, (tile + u) * kThreads + tid, cur[u]);
+    }
+    for (; tile + U <= full_tiles; tile += step) {
+      const uint64_t next = tile + step;
+      const bool more = next + U <= full_tiles;  // uniform across the workgroup
+      RawChunk<DT, PT> nxt[U];
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_raw<DT, PT>(prm.R, (next + u) * kThreads + tid, nxt[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the next loads go out before this work
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float g[kVec];
-        sum_raw<DT, PT>(raw[u], prm.inv_scale, g);
+        sum_raw<DT, PT>(cur[u], prm.inv_scale, g);
         if (WRITE) store_g_tile(prm.g_out, (tile + u) * kThreads + tid, g);
         if constexpr (NORM) norm_chunk(g);
       }
-    } else {
+      if (more) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float g[kVec];
-        reduce_chunk<DT, PT>(prm.R, prm.P, (tile + u) * kThreads + tid, true, prm.n,
-                             prm.inv_scale, g);
-        if (WRITE) store_f32_chunk<true>(prm.g_out, (tile + u) * kThreads + tid, true, prm.n, g);
-        if constexpr (NORM) norm_chunk(g);
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      }
+    }
+  } else {
+    for (; tile + U <= full_tiles; tile += step) {
+      if constexpr (PT > 0) {
+        RawChunk<DT, PT> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_raw<DT, PT>(prm.R, (tile + u) * kThreads + tid, raw[u]);
+        __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first wait
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float g[kVec];
+          sum_raw<DT, PT>(raw[u], prm.inv_scale, g);
+          if (WRITE) store_g_tile(prm.g_out, (tile + u) * kThreads + tid, g);
+          if constexpr (NORM) norm_chunk(g);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float g[kVec];
+          reduce_chunk<DT, PT>(prm.R, prm.P, (tile + u) * kThreads + tid, true, prm.n,
+                               prm.inv_scale, g);
+          if (WRITE)
+            store_f32_chunk<true>(prm.g_out, (tile + u) * kThreads + tid, true, prm.n, g);
+          if constexpr (NORM) norm_chunk(g);
+        }
       }
     }
   }
@@ -176,29 +257,46 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
   }
 }
 
-template <int DT, int PT>
-static void reduce_dispatch_io(const ReduceParams& prm, bool write, bool norm, unsigned grid,
-                               hipStream_t st) {
+template <int DT, int PT, bool PIPE>
+static void reduce_launch(const ReduceParams& prm, bool write, bool norm, unsigned grid,
+                          hipStream_t st) {
   if (write && norm)
-    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, true>), dim3(grid), dim3(kThreads), 0,
-                       st, prm);
+    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, true, PIPE>), dim3(grid),
+                       dim3(kThreads), 0, st, prm);
   else if (write)
-    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, false>), dim3(grid), dim3(kThreads),
-                       0, st, prm);
+    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, false, PIPE>), dim3(grid),
+                       dim3(kThreads), 0, st, prm);
   else
-    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, false, true>), dim3(grid), dim3(kThreads),
-                       0, st, prm);
+    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, false, true, PIPE>), dim3(grid),
+                       dim3(kThreads), 0, st, prm);
+}
+
+// Below ZS_REDUCE_PIPE_MAX_ELEMS elements (a bucket) the pipelined form on
+// one workgroup per CU measured faster with 4 or 8 replicas; above it (a whole
+// multi-GB shard) the unpipelined form on ZS_REDUCE_BLOCKS_PER_CU did.  Both
+// compute the same bits.
+template <int DT, int PT>
+static void reduce_dispatch_io(const ReduceParams& prm, bool write, bool norm,
+                               hipStream_t st) {
+  if constexpr (PT >= 4) {
+    if (prm.n <= static_cast<uint64_t>(ZS_REDUCE_PIPE_MAX_ELEMS)) {
+      reduce_launch<DT, PT, true>(prm, write, norm,
+                                  grid_for(prm.nchunks, ZS_REDUCE_PIPE_BLOCKS_PER_CU), st);
+      return;
+    }
+  }
+  reduce_launch<DT, PT, false>(prm, write, norm,
+                               grid_for(prm.nchunks, ZS_REDUCE_BLOCKS_PER_CU), st);
 }
 
 template <int DT>
-static void reduce_dispatch_p(const ReduceParams& prm, bool write, bool norm, unsigned grid,
-                              hipStream_t st) {
+static void reduce_dispatch_p(const ReduceParams& prm, bool write, bool norm, hipStream_t st) {
   switch (prm.P) {
-    case 1: reduce_dispatch_io<DT, 1>(prm, write, norm, grid, st); break;
-    case 2: reduce_dispatch_io<DT, 2>(prm, write, norm, grid, st); break;
-    case 4: reduce_dispatch_io<DT, 4>(prm, write, norm, grid, st); break;
-    case 8: reduce_dispatch_io<DT, 8>(prm, write, norm, grid, st); break;
-    default: reduce_dispatch_io<DT, 0>(prm, write, norm, grid, st); break;
+    case 1: reduce_dispatch_io<DT, 1>(prm, write, norm, st); break;
+    case 2: reduce_dispatch_io<DT, 2>(prm, write, norm, st); break;
+    case 4: reduce_dispatch_io<DT, 4>(prm, write, norm, st); break;
+    case 8: reduce_dispatch_io<DT, 8>(prm, write, norm, st); break;
+    default: reduce_dispatch_io<DT, 0>(prm, write, norm, st); break;
   }
 }
 
@@ -215,14 +313,13 @@ hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t
   prm.nchunks = (n + kVec - 1) / kVec;
   prm.g_out = g_out;
   prm.acc = acc;
-  const unsigned grid = grid_for(prm.nchunks, ZS_REDUCE_BLOCKS_PER_CU);
   const bool write = g_out != nullptr, norm = acc != nullptr;
   if (dtype == ZERO_BF16)
-    reduce_dispatch_p<ZERO_BF16>(prm, write, norm, grid, stream);
+    reduce_dispatch_p<ZERO_BF16>(prm, write, norm, stream);
   else if (dtype == ZERO_MXFP8)
-    reduce_dispatch_p<ZERO_MXFP8>(prm, write, norm, grid, stream);
+    reduce_dispatch_p<ZERO_MXFP8>(prm, write, norm, stream);
   else
-    reduce_dispatch_p<ZERO_F32>(prm, write, norm, grid, stream);
+    reduce_dispatch_p<ZERO_F32>(prm, write, norm, stream);
   return hipGetLastError();
 }
 
@@ -376,27 +473,35 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
   }
 }
 
+template <int SRC, int PT, bool PARAM, bool MX>
+static void adamw_launch(const AdamParams& prm, hipStream_t st) {
+  const auto kernel = adamw_kernel<SRC, PT, PARAM, MX>;
+  const int per_cu =
+      resident_per_cu(reinterpret_cast<const void*>(kernel), ZS_ADAMW_BLOCKS_PER_CU);
+  hipLaunchKernelGGL(kernel, dim3(grid_for(prm.nchunks, per_cu)), dim3(kThreads), 0, st, prm);
+}
+
 template <int SRC, int PT>
-static void adamw_dispatch_param(const AdamParams& prm, unsigned grid, hipStream_t st) {
+static void adamw_dispatch_param(const AdamParams& prm, hipStream_t st) {
   const bool param = prm.param != nullptr, mx = prm.mx_elem != nullptr;
   if (mx && param)
-    hipLaunchKernelGGL((adamw_kernel<SRC, PT, true, true>), dim3(grid), dim3(kThreads), 0, st, prm);
+    adamw_launch<SRC, PT, true, true>(prm, st);
   else if (mx)
-    hipLaunchKernelGGL((adamw_kernel<SRC, PT, false, true>), dim3(grid), dim3(kThreads), 0, st, prm);
+    adamw_launch<SRC, PT, false, true>(prm, st);
   else if (param)
-    hipLaunchKernelGGL((adamw_kernel<SRC, PT, true, false>), dim3(grid), dim3(kThreads), 0, st, prm);
+    adamw_launch<SRC, PT, true, false>(prm, st);
   else
-    hipLaunchKernelGGL((adamw_kernel<SRC, PT, false, false>), dim3(grid), dim3(kThreads), 0, st, prm);
+    adamw_launch<SRC, PT, false, false>(prm, st);
 }
 
 template <int DT>
-static void adamw_dispatch_p(const AdamParams& prm, unsigned grid, hipStream_t st) {
+static void adamw_dispatch_p(const AdamParams& prm, hipStream_t st) {
   switch (prm.P) {
-    case 1: adamw_dispatch_param<DT, 1>(prm, grid, st); break;
-    case 2: adamw_dispatch_param<DT, 2>(prm, grid, st); break;
-    case 4: adamw_dispatch_param<DT, 4>(prm, grid, st); break;
-    case 8: adamw_dispatch_param<DT, 8>(prm, grid, st); break;
-    default: adamw_dispatch_param<DT, 0>(prm, grid, st); break;
+    case 1: adamw_dispatch_param<DT, 1>(prm, st); break;
+    case 2: adamw_dispatch_param<DT, 2>(prm, st); break;
+    case 4: adamw_dispatch_param<DT, 4>(prm, st); break;
+    case 8: adamw_dispatch_param<DT, 8>(prm, st); break;
+    default: adamw_dispatch_param<DT, 0>(prm, st); break;
   }
 }
 
@@ -420,13 +525,12 @@ hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream) {
   prm.n = a.n;
   prm.nchunks = (a.n + kVec - 1) / kVec;
   prm.s = a.s;
-  const unsigned grid = grid_for(prm.nchunks, ZS_ADAMW_BLOCKS_PER_CU);
   if (a.grad != nullptr)
-    adamw_dispatch_param<-1, 1>(prm, grid, stream);
+    adamw_dispatch_param<-1, 1>(prm, stream);
   else if (a.dtype == ZERO_BF16)
-    adamw_dispatch_p<ZERO_BF16>(prm, grid, stream);
+    adamw_dispatch_p<ZERO_BF16>(prm, stream);
   else
-    adamw_dispatch_p<ZERO_F32>(prm, grid, stream);
+    adamw_dispatch_p<ZERO_F32>(prm, stream);
   return hipGetLastError();
 }
 
