@@ -60,6 +60,9 @@ def parse():
                     help="skip the offload bill (PCIe copies + all-cores CPU AdamW)")
     ap.add_argument("--cpu-threads", type=int, default=16,
                     help="threads of the all-cores oracle legs (capped by the host)")
+    ap.add_argument("--no-recycle", action="store_true",
+                    help="allocate the workload without first writing and releasing a "
+                         "scratch allocation of its size")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused single-operation chain")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -336,6 +339,35 @@ def cpu_baseline_leg(w, args, threads, gpu_step_ms, reduce_ms):
     return res
 
 
+def workload_bytes(w):
+    """Device bytes the workload allocates: the P replicas, fp32 master/m/v
+    and g, bf16 param and the MXFP8 outputs."""
+    g_b = MX_BYTES if w.mx_grads else w.g_bytes
+    per = 4 * 4 + 2 + (MX_BYTES if w.pack else 0)
+    return int(w.S * (w.P * g_b + per))
+
+
+def recycle_device_memory(dev, nbytes):
+    """Untimed set-up: write and release a scratch allocation somewhat larger
+    than the workload before the workload allocates.  On a freshly booted
+    MI355X, device memory that no allocation had written before ran the
+    write-heavy AdamW pass about 15 % slower for the whole life of the process
+    (the first process on a box); memory that had been written and released
+    (by an earlier process, or by this scratch) did not.  Returns the scratch
+    size in bytes."""
+    import torch
+    free, _ = torch.cuda.mem_get_info(dev)
+    size = min(int(nbytes * 1.1) + (1 << 30), free - (4 << 30))
+    if size <= 0:
+        return 0
+    x = torch.empty(size, dtype=torch.uint8, device=dev)
+    x.fill_(0)
+    torch.cuda.synchronize(dev)
+    del x
+    torch.cuda.empty_cache()
+    return size
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -361,6 +393,7 @@ def main():
     w = configs.ALL[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    recycled = None if args.no_recycle else recycle_device_memory(dev, workload_bytes(w))
     grad_dtype = "mxfp8" if w.mx_grads else (torch.bfloat16 if w.grad_bf16 else torch.float32)
     st = zs.ShardStep(w.S, w.P, grad_dtype, lr=w.lr,
                       beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
@@ -510,6 +543,8 @@ def main():
                    "max_norm": w.max_norm, "check_overflow": w.check_overflow,
                    "mxfp8_pack": ("fused into AdamW" if st.fuse_pack else "separate pass")
                    if w.pack else False, "path": st.path},
+        "memory_prep": (f"{recycled} B scratch written and released before allocating"
+                        if recycled else "none"),
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_param": sum(kinds.values()),
