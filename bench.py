@@ -371,8 +371,9 @@ def recycle_device_memory(dev, nbytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs each rank's shard step "
-              f"on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: it runs one rank's shard step on a "
+              f"single MI355X, and the exchanges between ranks are not implemented "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     if args.summarize_pmc:
