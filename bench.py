@@ -399,7 +399,8 @@ def main():
     st = zs.ShardStep(w.S, w.P, grad_dtype, lr=w.lr,
                       beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
                       max_norm=w.max_norm, check_overflow=w.check_overflow,
-                      loss_scale=w.loss_scale, bucket=w.bucket, pack=w.pack, device=dev)
+                      loss_scale=w.loss_scale, bucket=w.bucket, pack=w.pack,
+                      device_counter=True, device=dev)
     start = w.shard_start()
     synth.fill_device(w.master_spec(), start, st.master)
     synth.fill_device(w.master_spec(), start, st.param)
@@ -486,7 +487,9 @@ def main():
     unfused = None
     if not args.no_unfused and not w.mx_grads:
         # The same step as a chain of single-operation kernels, same process
-        # and buffers: what fusion saves (bit-identical results).
+        # and buffers: what fusion saves (bit-identical results).  The chain
+        # takes the host step counter.
+        st.set_counter(device=False)
         for _ in range(max(1, args.warmup)):
             st.step_unfused(reps)
         torch.cuda.synchronize()
@@ -500,7 +503,7 @@ def main():
                    "hbm_gbps": round(ub * w.S / (u_ms * 1e-3) / 1e9, 1),
                    "launches_per_step": 11 + (1 if w.pack else 0),
                    "fused_speedup": round(u_ms / (1e3 * elapsed / args.steps), 3)}
-        st.applied_steps()
+        st.set_counter(device=True)
 
     # Cold steps for workloads whose step fits in the caches (L2 4 MB per XCD,
     # 256 MB MALL): a 1 GiB scratch write before each step evicts the state,
@@ -528,6 +531,30 @@ def main():
                 "hbm_gbps": round(sum(kinds.values()) * w.S / (cold_ms * 1e-3) / 1e9, 1),
                 "note": "1 GiB scratch write before each step (evicts L2 and MALL)"}
         st.applied_steps()
+
+    # The same small steps recorded once as a graph and replayed: what the
+    # host's launches cost per step.  Timed by events around each replay.
+    graph_steps = None
+    if sum(kinds.values()) * w.S < (2 << 30):
+        graph = st.capture(reps)
+        graph.replay()
+        torch.cuda.synchronize()
+        g_ev = []
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            graph.replay()
+            b.record()
+            g_ev.append((a, b))
+        torch.cuda.synchronize()
+        g_wall = 1e3 * (time.perf_counter() - g0) / args.steps
+        g_ms = statistics.median(a.elapsed_time(b) for a, b in g_ev)
+        graph_steps = {"step_ms_median": round(g_ms, 4), "wall_ms_per_step": round(g_wall, 4),
+                       "params_per_s": round(w.S / (g_wall * 1e-3), 1),
+                       "note": "one recorded step (all its launches) replayed per step"}
+        del graph
 
     ms_per_step = 1e3 * elapsed / args.steps
     step_bytes = sum(kinds.values()) * w.S
@@ -561,6 +588,7 @@ def main():
         "step_ms_median": round(statistics.median(step_ms), 4),
         "step_ms_p90": round(p90, 4),
         "cold_steps": cold,
+        "graph_steps": graph_steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

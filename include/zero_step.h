@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ZERO_ABI_VERSION 2
+#define ZERO_ABI_VERSION 3
 #define ZERO_MAX_REPLICAS 64
 
 /* Element types of gradient replicas.  ZERO_MXFP8 replicas (E4M3 codes plus
@@ -166,6 +166,14 @@ typedef struct zero_adamw_args {
   int32_t *skipped_out;        /* device int: 1 skipped, 0 applied; or NULL */
   uint8_t *mx_elem_out;        /* uint8[n]: MXFP8 codes of the new params,  */
   uint8_t *mx_scale_out;       /* uint8[n/32]: their scales; both or NULL   */
+  int64_t *step_dev;           /* device int64, 8-byte aligned, or NULL:    */
+                               /* the count t of updates applied so far.    */
+                               /* When set, `step` is ignored, this call    */
+                               /* applies update t + 1 with scalars derived */
+                               /* on the device, and t advances by one on   */
+                               /* the device unless the gate skips.  No     */
+                               /* host round trip is left in the step, so a */
+                               /* whole step can be captured in a graph.    */
 } zero_adamw_args;
 
 /* Fused AdamW step on n elements of fp32 master/m/v.
@@ -190,7 +198,11 @@ typedef struct zero_adamw_args {
  * With mx_elem_out/mx_scale_out set (n % 32 == 0, else ZERO_ESIZE) the same
  * pass also writes the MXFP8 pack of the new bf16 params, bit for bit what
  * zero_mxfp8_pack would produce from param_bf16, without reading it back.
- * A skipped step writes none of the outputs. */
+ * A skipped step writes none of the outputs.
+ * With step_dev set, every workgroup derives the scalars above from the
+ * counter it reads, in the same binary64 operations, so the bits equal those
+ * of the host-counter form; a one-lane kernel queued after the update then
+ * re-evaluates the gate and advances the counter if the step applied. */
 int zero_adamw_step(const zero_adamw_args *args, void *stream);
 
 /* The gate alone, for inspection: writes *coef_out (device float) and
@@ -220,8 +232,8 @@ int zero_mxfp8_pack(const uint16_t *bf16_in, size_t n, uint8_t *elem_out,
  * the fused path, only the HBM traffic and launches differ.
  *   args       as for zero_adamw_step, except that `accs`/`n_accs` hold
  *              only the OTHER ranks' accumulators (this rank's own norm is
- *              computed inside the chain), and MXFP8 outputs need
- *              param_bf16.
+ *              computed inside the chain), MXFP8 outputs need param_bf16,
+ *              and the step index comes from `step` (step_dev must be NULL).
  *   workspace  device scratch of at least zero_unfused_workspace_bytes(n,
  *              n_accs) bytes, 256-byte aligned; contents are overwritten.
  * ZERO_ESIZE if workspace_bytes is too small. */

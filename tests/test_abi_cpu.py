@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.zero_abi_version.restype = C.c_int
-    assert lib.zero_abi_version() == 2
+    assert lib.zero_abi_version() == 3
     lib.zero_strerror.restype = C.c_char_p
     lib.zero_strerror.argtypes = [C.c_int]
     texts = {lib.zero_strerror(s).decode() for s in (0, -1, -2, -3, -4, 7)}
@@ -85,3 +85,24 @@ def test_argument_checks(lib):
     assert lib.zero_unfused_workspace_bytes(1000, 2) >= 2 * 4000 + 3 * 64
     lib.zero_adamw_step_unfused.argtypes = [vp, vp, C.c_size_t, vp]
     assert lib.zero_adamw_step_unfused(None, fake, 1 << 20, None) == -1
+
+
+def test_adamw_step_counter_checks(lib):
+    """The step index: a host `step` >= 1, or a device counter (8-byte
+    aligned); the unfused chain takes the host form only.  Every case here
+    fails its checks, so nothing is launched."""
+    from zero_sharded_mixed_step_amd._binding import _AdamArgs
+    vp = C.c_void_p
+    lib.zero_adamw_step.argtypes = [vp, vp]
+    lib.zero_adamw_step_unfused.argtypes = [vp, vp, C.c_size_t, vp]
+    fake = 0x10000
+    a = _AdamArgs()
+    a.n, a.grad_f32, a.P, a.dtype = 64, fake, 1, 0
+    a.master, a.m, a.v = fake + 0x1000, fake + 0x2000, fake + 0x3000
+    a.lr, a.beta1, a.beta2, a.eps = 1e-3, 0.9, 0.999, 1e-8
+    a.step, a.step_dev = 0, None
+    assert lib.zero_adamw_step(C.byref(a), None) == -1          # no step at all
+    a.step_dev = fake + 4
+    assert lib.zero_adamw_step(C.byref(a), None) == -2          # counter misaligned
+    a.step_dev = fake + 8
+    assert lib.zero_adamw_step_unfused(C.byref(a), fake, 1 << 30, None) == -1

@@ -653,3 +653,87 @@ def test_zero_length_calls_touch_nothing(zs):
     assert torch.all(v == 0.75).item() and torch.all(param == 0x1234).item()
     assert torch.all(elem == 0xAB).item() and torch.all(scale == 0xCD).item()
     assert torch.all(g == 7.0).item()
+
+
+# ------------------------------------------- device step counter, graphs --
+
+_HP = dict(lr=3e-4, beta1=0.85, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+           check_overflow=True, pack=True)
+_STATE = ("master", "m", "v", "param", "mx_elem", "mx_scale")
+
+
+def _same_state(a, b):
+    import torch
+    return all(torch.equal(getattr(a, k).view(torch.uint8), getattr(b, k).view(torch.uint8))
+               for k in _STATE)
+
+
+def _fill_grads(reps, call, inject_call):
+    for k, r in enumerate(reps):
+        synth.fill_device(synth.make_spec(seed=4, cfg=60, stream=1, step=call, replica=k,
+                                          sigma=1e-3, outlier_rate=0.01, outlier_mult=100.0),
+                          0, r)
+    if call == inject_call:
+        reps[2][77] = 0x7F80                   # +inf in one replica: the step is skipped
+
+
+def _init(*steps):
+    mspec = synth.make_spec(seed=4, cfg=60, stream=0, sigma=0.02)
+    for st in steps:
+        synth.fill_device(mspec, 0, st.master)
+        synth.fill_device(mspec, 0, st.param)
+        st.mx_elem.zero_()
+        st.mx_scale.zero_()
+
+
+def test_device_counter_matches_host_counter(zs):
+    """The device counter (scalars derived on the device from the counter,
+    advanced on the device unless the gate skips) gives the bits of the
+    host-counter step, through a skipped call and at a large step index."""
+    import torch
+    n, P = 65536 + 96, 8
+    host = zs.ShardStep(n, P, torch.bfloat16, **_HP)
+    dev = zs.ShardStep(n, P, torch.bfloat16, device_counter=True, **_HP)
+    _init(host, dev)
+    reps = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(P)]
+    for call in range(1, 13):
+        _fill_grads(reps, call, inject_call=5)
+        host.step(reps)
+        dev.step(reps)
+        torch.cuda.synchronize()
+        assert _same_state(host, dev), call
+    assert host.applied_steps() == dev.applied_steps() == 11
+    host.t = 99_999
+    dev.t_dev.fill_(99_999)
+    _fill_grads(reps, 13, inject_call=0)
+    host.step(reps)
+    dev.step(reps)
+    torch.cuda.synchronize()
+    assert _same_state(host, dev)
+    assert host.applied_steps() == dev.applied_steps() == 100_000
+
+
+def test_graph_replay_matches_eager(zs):
+    """One step (35-odd bucketed reduce launches, gated AdamW, fused MXFP8)
+    recorded once and replayed: after every replay, with eager work and
+    synchronisation between replays, the state is bitwise that of the same
+    step run eagerly, including a skipped replay."""
+    import torch
+    n, P = 65536 + 96, 8
+    eager = zs.ShardStep(n, P, torch.bfloat16, device_counter=True, bucket=32 * 61, **_HP)
+    graphed = zs.ShardStep(n, P, torch.bfloat16, device_counter=True, bucket=32 * 61, **_HP)
+    _init(eager, graphed)
+    reps = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(P)]
+    _fill_grads(reps, 1, inject_call=0)
+    torch.cuda.synchronize()
+    g = graphed.capture(reps)                  # records; runs nothing
+    torch.cuda.synchronize()
+    assert graphed.applied_steps() == 0 and _same_state(eager, graphed)
+    for call in range(1, 8):
+        _fill_grads(reps, call, inject_call=4)
+        eager.step(reps)
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same_state(eager, graphed), call
+        assert eager.applied_steps() == graphed.applied_steps()
+    assert graphed.applied_steps() == 6

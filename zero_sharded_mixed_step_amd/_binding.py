@@ -13,6 +13,7 @@ import torch
 from . import build as _build
 
 ZERO_F32, ZERO_BF16, ZERO_MXFP8 = 0, 1, 2
+ABI_VERSION = 3        # the zero_step.h this binding's structs follow
 ZERO_MAX_REPLICAS = 64
 ACC_WORDS = 8          # one zero_norm_acc = 64 bytes = 8 int64 words
 
@@ -34,7 +35,7 @@ class _AdamArgs(C.Structure):
                 ("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
                 ("skipped_out", C.c_void_p), ("mx_elem_out", C.c_void_p),
-                ("mx_scale_out", C.c_void_p)]
+                ("mx_scale_out", C.c_void_p), ("step_dev", C.c_void_p)]
 
 
 def lib():
@@ -66,6 +67,9 @@ def lib():
                   L.zero_adamw_step, L.zero_step_gate, L.zero_mxfp8_pack,
                   L.zero_adamw_step_unfused):
             f.restype = i
+        if L.zero_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{_build.LIB} has ABI version {L.zero_abi_version()}, the "
+                               f"binding expects {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -223,7 +227,7 @@ def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:
 
 def _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32, replicas,
                inv_scale, param_bf16, accs, max_norm, check_overflow, skipped_out, mx_elem_out,
-               mx_scale_out, n):
+               mx_scale_out, n, step_dev=None):
     n = master.numel() if n is None else int(n)
     for name, t in (("master", master), ("m", m), ("v", v), ("grad_f32", grad_f32)):
         _need(t, n, name, F32)
@@ -236,6 +240,7 @@ def _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32
     _need(skipped_out, 1, "skipped_out", I32)
     _need(mx_elem_out, n, "mx_elem_out", U8)
     _need(mx_scale_out, n // 32, "mx_scale_out", U8)
+    _need(step_dev, 1, "step_dev", (torch.int64,))
     a = _AdamArgs()
     a.n = n
     keep = None
@@ -261,17 +266,21 @@ def _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32
     a.skipped_out = _dev_ptr(skipped_out, "skipped_out")
     a.mx_elem_out = _dev_ptr(mx_elem_out, "mx_elem_out")
     a.mx_scale_out = _dev_ptr(mx_scale_out, "mx_scale_out")
+    a.step_dev = _dev_ptr(step_dev, "step_dev")
     return a, keep
 
 
-def zero_adamw_step(master, m, v, *, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+def zero_adamw_step(master, m, v, *, step=0, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                     weight_decay=0.0, grad_f32=None, replicas=None, inv_scale=1.0,
                     param_bf16=None, accs=None, max_norm=0.0, check_overflow=False,
                     skipped_out=None, mx_elem_out=None, mx_scale_out=None, n=None,
-                    stream=None) -> None:
+                    step_dev=None, stream=None) -> None:
+    """`step`: 1-based index of this applied update; or `step_dev`: an int64
+    device tensor holding the count of updates applied so far, read and
+    advanced on the device (then `step` is ignored)."""
     a, keep = _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32,
                          replicas, inv_scale, param_bf16, accs, max_norm, check_overflow,
-                         skipped_out, mx_elem_out, mx_scale_out, n)
+                         skipped_out, mx_elem_out, mx_scale_out, n, step_dev)
     rc = lib().zero_adamw_step(C.byref(a), _stream(stream))
     del keep
     _check(rc, "zero_adamw_step")

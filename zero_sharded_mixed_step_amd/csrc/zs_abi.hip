@@ -29,35 +29,6 @@ int check_replicas(const void* const* replicas, int P, int dtype) {
   return ZERO_OK;
 }
 
-// beta^t by square-and-multiply over the bits of t, least significant bit
-// first, in binary64 (the fixed evaluation order the step's scalars use).
-double power_lsb_first(double beta, int64_t t) {
-  double acc = 1.0;
-  double sq = beta;
-  for (uint64_t e = static_cast<uint64_t>(t); e != 0; e >>= 1) {
-    if (e & 1u) acc = acc * sq;
-    sq = sq * sq;
-  }
-  return acc;
-}
-
-zs::AdamScalars derive_scalars(double lr, double beta1, double beta2, double eps, double wd,
-                               int64_t t) {
-  zs::AdamScalars s;
-  s.b1 = static_cast<float>(beta1);
-  s.b2 = static_cast<float>(beta2);
-  s.omb1 = static_cast<float>(1.0 - beta1);
-  s.omb2 = static_cast<float>(1.0 - beta2);
-  const double bias1 = 1.0 - power_lsb_first(beta1, t);
-  const double bias2 = 1.0 - power_lsb_first(beta2, t);
-  s.step_size = static_cast<float>(lr / bias1);
-  s.sqrt_bc2 = static_cast<float>(std::sqrt(bias2));
-  const double lw = lr * wd;
-  s.decay = static_cast<float>(1.0 - lw);
-  s.eps = static_cast<float>(eps);
-  return s;
-}
-
 }  // namespace
 
 extern "C" {
@@ -163,7 +134,9 @@ int adamw_args_to_launch(const zero_adamw_args* a, zs::AdamLaunch& L) {
   if (a == nullptr) return ZERO_EINVAL;
   if (a->master == nullptr || a->m == nullptr || a->v == nullptr) return ZERO_EINVAL;
   if ((a->grad_f32 == nullptr) == (a->replicas == nullptr)) return ZERO_EINVAL;
-  if (a->step < 1 || a->n_accs < 0 || (a->n_accs > 0 && a->accs == nullptr)) return ZERO_EINVAL;
+  if ((a->step_dev == nullptr && a->step < 1) || a->n_accs < 0 ||
+      (a->n_accs > 0 && a->accs == nullptr))
+    return ZERO_EINVAL;
   if (a->replicas != nullptr) {
     const int rc = check_replicas(a->replicas, a->P, a->dtype);
     if (rc != ZERO_OK) return rc;
@@ -173,7 +146,8 @@ int adamw_args_to_launch(const zero_adamw_args* a, zs::AdamLaunch& L) {
       (a->param_bf16 && !aligned16(a->param_bf16)) || (a->accs && !aligned16(a->accs)) ||
       (a->skipped_out && !aligned4(a->skipped_out)) ||
       (a->mx_elem_out && !aligned16(a->mx_elem_out)) ||
-      (a->mx_scale_out && !aligned16(a->mx_scale_out)))
+      (a->mx_scale_out && !aligned16(a->mx_scale_out)) ||
+      (a->step_dev && (reinterpret_cast<uintptr_t>(a->step_dev) & 7u) != 0))
     return ZERO_EALIGN;
   if ((a->mx_elem_out == nullptr) != (a->mx_scale_out == nullptr)) return ZERO_EINVAL;
   if (a->mx_elem_out != nullptr && a->n % 32 != 0) return ZERO_ESIZE;
@@ -194,7 +168,9 @@ int adamw_args_to_launch(const zero_adamw_args* a, zs::AdamLaunch& L) {
   L.check_overflow = a->check_overflow;
   L.skipped_out = a->skipped_out;
   L.n = a->n;
-  L.s = derive_scalars(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
+  L.h = zs::AdamHyper{a->lr, a->beta1, a->beta2, a->eps, a->weight_decay};
+  L.step_dev = a->step_dev;
+  L.s = zs::derive_adam_scalars(L.h, a->step_dev ? 1 : a->step);
   return ZERO_OK;
 }
 
@@ -207,7 +183,7 @@ int zero_adamw_step(const zero_adamw_args* a, void* stream) {
     zs::AdamLaunch L;
     const int rc = adamw_args_to_launch(a, L);
     if (rc != ZERO_OK) return rc;
-    if (a->n == 0 && a->skipped_out == nullptr) return ZERO_OK;
+    if (a->n == 0 && a->skipped_out == nullptr && a->step_dev == nullptr) return ZERO_OK;
     return status_of(zs::launch_adamw(L, as_stream(stream)));
   } catch (...) {
     return ZERO_EHIP;
@@ -225,6 +201,7 @@ int zero_adamw_step_unfused(const zero_adamw_args* a, void* workspace, size_t wo
     const int rc = adamw_args_to_launch(a, L);
     if (rc != ZERO_OK) return rc;
     if (a->mx_elem_out != nullptr && a->param_bf16 == nullptr) return ZERO_EINVAL;
+    if (a->step_dev != nullptr) return ZERO_EINVAL;  // the chain takes the host counter
     if (a->n >= (size_t(1) << 32)) return ZERO_ESIZE;  // the chain's own norm accumulator
     if (workspace == nullptr) return ZERO_EINVAL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ZERO_EALIGN;

@@ -14,6 +14,44 @@ struct AdamScalars {
   float b1, b2, omb1, omb2, step_size, sqrt_bc2, decay, eps;
 };
 
+// The AdamW hyperparameters as the caller gives them (binary64).
+struct AdamHyper {
+  double lr, beta1, beta2, eps, wd;
+};
+
+// beta^t by square-and-multiply over the bits of t, least significant bit
+// first, in binary64 (the fixed evaluation order of the step's scalars).
+__host__ __device__ inline double power_lsb_first(double beta, int64_t t) {
+  double acc = 1.0;
+  double sq = beta;
+  for (uint64_t e = static_cast<uint64_t>(t); e != 0; e >>= 1) {
+    if (e & 1u) acc = acc * sq;
+    sq = sq * sq;
+  }
+  return acc;
+}
+
+// The per-step binary32 scalars of update t, each computed in binary64 and
+// rounded once.  Host and device evaluate the same correctly rounded binary64
+// operations (+, -, *, /, sqrt; nothing contracted), so both give the same
+// bits: the device derives them itself when the step counter lives in device
+// memory.
+__host__ __device__ inline AdamScalars derive_adam_scalars(const AdamHyper& h, int64_t t) {
+  AdamScalars s;
+  s.b1 = static_cast<float>(h.beta1);
+  s.b2 = static_cast<float>(h.beta2);
+  s.omb1 = static_cast<float>(1.0 - h.beta1);
+  s.omb2 = static_cast<float>(1.0 - h.beta2);
+  const double bias1 = 1.0 - power_lsb_first(h.beta1, t);
+  const double bias2 = 1.0 - power_lsb_first(h.beta2, t);
+  s.step_size = static_cast<float>(h.lr / bias1);
+  s.sqrt_bc2 = static_cast<float>(__builtin_sqrt(bias2));
+  const double lw = h.lr * h.wd;
+  s.decay = static_cast<float>(1.0 - lw);
+  s.eps = static_cast<float>(h.eps);
+  return s;
+}
+
 // Workgroups (of 256 threads) per compute unit of each persistent grid,
 // from sweeps of 1..10 on MI355X: the reduce pass needs 4 to keep enough
 // loads in flight, except for bucket-sized launches with 4 or 8 replicas,
@@ -58,7 +96,9 @@ struct AdamLaunch {
   int check_overflow;
   int32_t* skipped_out;
   uint64_t n;
-  AdamScalars s;
+  AdamScalars s;         // update `step` (host counter)
+  AdamHyper h;
+  int64_t* step_dev;     // or: the device counter of applied updates
 };
 
 hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream);

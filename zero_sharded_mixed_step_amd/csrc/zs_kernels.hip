@@ -352,7 +352,9 @@ struct AdamParams {
   int32_t* skipped_out;
   uint64_t n;
   uint64_t nchunks;
-  AdamScalars s;
+  AdamScalars s;             // scalars of the host-counted update, or
+  AdamHyper h;               // hyperparameters to derive them from
+  const int64_t* step_dev;   // the device counter of applied updates
 };
 
 #ifndef ZS_ADAMW_UNROLL
@@ -365,16 +367,18 @@ struct AdamParams {
 template <int SRC, int PT, bool PARAM, bool MX>
 __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
   __shared__ Gate s_gate;
+  __shared__ AdamScalars s_sc;
   if (threadIdx.x == 0) {
     const Gate gt = evaluate_gate(prm.accs, prm.n_accs, prm.max_norm, prm.check_overflow);
     s_gate = gt;
+    s_sc = prm.step_dev != nullptr ? derive_adam_scalars(prm.h, *prm.step_dev + 1) : prm.s;
     if (blockIdx.x == 0 && prm.skipped_out != nullptr) *prm.skipped_out = gt.skip;
   }
   __syncthreads();
   const Gate gt = s_gate;
   if (gt.skip) return;
   const float coef = gt.coef;
-  const AdamScalars sc = prm.s;
+  const AdamScalars sc = s_sc;
   const float neg_step = -sc.step_size;
   // The update of one chunk from its loaded g and state; stores the new
   // state and param and leaves the param bits in pb (for the MXFP8 epilogue).
@@ -505,6 +509,17 @@ static void adamw_dispatch_p(const AdamParams& prm, hipStream_t st) {
   }
 }
 
+// Device step counter: after the update, count it as applied unless the
+// gate (the same evaluation the update made) skipped it.  Runs after every
+// workgroup of the update has read the counter (stream order).
+__global__ void step_advance_kernel(int64_t* step_dev, const zero_norm_acc* accs, int n_accs,
+                                    double max_norm, int check_overflow) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const Gate g = evaluate_gate(accs, n_accs, max_norm, check_overflow);
+    if (!g.skip) *step_dev += 1;
+  }
+}
+
 hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream) {
   AdamParams prm;
   prm.R = a.replicas ? pack_replicas(a.replicas, a.P) : Replicas{};
@@ -525,12 +540,17 @@ hipError_t launch_adamw(const AdamLaunch& a, hipStream_t stream) {
   prm.n = a.n;
   prm.nchunks = (a.n + kVec - 1) / kVec;
   prm.s = a.s;
+  prm.h = a.h;
+  prm.step_dev = a.step_dev;
   if (a.grad != nullptr)
     adamw_dispatch_param<-1, 1>(prm, stream);
   else if (a.dtype == ZERO_BF16)
     adamw_dispatch_p<ZERO_BF16>(prm, stream);
   else
     adamw_dispatch_p<ZERO_F32>(prm, stream);
+  if (a.step_dev != nullptr)
+    hipLaunchKernelGGL(step_advance_kernel, dim3(1), dim3(64), 0, stream, a.step_dev, a.accs,
+                       a.n_accs, a.max_norm, a.check_overflow);
   return hipGetLastError();
 }
 

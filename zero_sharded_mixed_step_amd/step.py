@@ -25,6 +25,10 @@ Step counter: `t` counts applied updates.  With the overflow check on, the
 device decides the skip; the flag travels to pinned host memory behind an
 event and is read just before the next step's AdamW launch, after that
 step's reduce work is already queued, so the GPU never waits on the host.
+With `device_counter=True` the counter lives in device memory instead: the
+AdamW kernel derives its scalars from it and a one-lane kernel advances it
+when the step applies, so a step needs nothing from the host and `capture()`
+can record it once as a graph that is replayed every step.
 """
 from typing import List, Optional
 
@@ -39,7 +43,8 @@ class ShardStep:
                  weight_decay: float = 0.0, max_norm: float = 0.0,
                  check_overflow: bool = False, loss_scale: float = 1.0,
                  bucket: Optional[int] = None, pack: bool = False,
-                 fuse_pack: bool = True, path: Optional[str] = None, device="cuda"):
+                 fuse_pack: bool = True, path: Optional[str] = None,
+                 device_counter: bool = False, device="cuda"):
         self.n, self.P = int(n), int(P)
         self.lr, self.beta1, self.beta2, self.eps, self.wd = lr, beta1, beta2, eps, weight_decay
         self.max_norm, self.check_overflow = float(max_norm), bool(check_overflow)
@@ -80,6 +85,9 @@ class ShardStep:
         self._skip_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
         self._skip_event = None
         self.t = 0
+        self.device_counter = bool(device_counter)
+        self.t_dev = (torch.zeros(1, dtype=torch.int64, device=dev)
+                      if self.device_counter else None)
         self.pack = pack
         self.fuse_pack = bool(pack and fuse_pack)
         if pack:
@@ -147,11 +155,15 @@ class ShardStep:
             kw["skipped_out"] = self.skipped
         if self.fuse_pack:
             kw["mx_elem_out"], kw["mx_scale_out"] = self.mx_elem, self.mx_scale
+        if self.device_counter:
+            kw["step_dev"] = self.t_dev
         if self.path == "materialize":
             B.zero_adamw_step(self.master, self.m, self.v, grad_f32=self.g, **kw)
         else:
             B.zero_adamw_step(self.master, self.m, self.v, replicas=replicas,
                               inv_scale=self.inv_scale, **kw)
+        if self.device_counter:
+            return
         if self.check_overflow:
             self._skip_host.copy_(self.skipped, non_blocking=True)
             self._skip_event = torch.cuda.Event()
@@ -170,6 +182,33 @@ class ShardStep:
         self.update(replicas, accs)
         if self.pack and not self.fuse_pack:
             self.pack_param()
+
+    def set_counter(self, device: bool) -> None:
+        """Move the count of applied updates between host and device memory
+        (waits for the work queued so far)."""
+        if device == self.device_counter:
+            return
+        if device:
+            self._resolve_pending_skip()
+            if self.t_dev is None:
+                self.t_dev = torch.zeros(1, dtype=torch.int64, device=self.master.device)
+            self.t_dev.fill_(self.t)
+        else:
+            self.t = int(self.t_dev.item())
+        self.device_counter = device
+
+    def capture(self, replicas: List[torch.Tensor],
+                accs: Optional[torch.Tensor] = None) -> "torch.cuda.CUDAGraph":
+        """Record one whole step (accumulator clear, reduce, gated AdamW with
+        the device counter, MXFP8 pack) as a graph; each `replay()` is one
+        step on the current contents of the same replica buffers.  Recording
+        runs nothing.  Needs device_counter=True (no host state per step)."""
+        if not self.device_counter:
+            raise ValueError("capture() needs device_counter=True")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step(replicas, accs)
+        return graph
 
     def step_unfused(self, replicas: List[torch.Tensor],
                      other_accs: Optional[torch.Tensor] = None) -> None:
@@ -190,6 +229,8 @@ class ShardStep:
             kw["skipped_out"] = self.skipped
         if self.pack:
             kw["mx_elem_out"], kw["mx_scale_out"] = self.mx_elem, self.mx_scale
+        if self.device_counter:
+            raise ValueError("the unfused chain takes the host step counter")
         B.zero_adamw_step_unfused(self.master, self.m, self.v, ws, **kw)
         if self.check_overflow:
             self._skip_host.copy_(self.skipped, non_blocking=True)
@@ -199,6 +240,9 @@ class ShardStep:
             self.t += 1
 
     def applied_steps(self) -> int:
-        """Applied updates so far (waits for the last skip flag)."""
+        """Applied updates so far (waits for the last skip flag, or reads the
+        device counter)."""
+        if self.device_counter:
+            return int(self.t_dev.item())
         self._resolve_pending_skip()
         return self.t
