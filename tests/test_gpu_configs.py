@@ -208,7 +208,7 @@ def _run_sampled(zs, w, calls, seed):
     import torch
     rng = np.random.default_rng(seed)
     idx = _sample_indices(w, rng)
-    st = _step_for(zs, w)
+    st = _step_for(zs, w, device_counter=True)     # as the benchmark runs the step
     _init_state(st, w, w.shard_start())
     reps = None
     for call in calls:
