@@ -348,16 +348,16 @@ def workload_bytes(w):
 
 
 def recycle_device_memory(dev, nbytes):
-    """Untimed set-up: write and release a scratch allocation somewhat larger
-    than the workload before the workload allocates.  On a freshly booted
-    MI355X, device memory that no allocation had written before ran the
-    write-heavy AdamW pass about 15 % slower for the whole life of the process
-    (the first process on a box); memory that had been written and released
-    (by an earlier process, or by this scratch) did not.  Returns the scratch
-    size in bytes."""
+    """Untimed set-up: write and release a scratch allocation of
+    max(150 GiB, 1.1 x the workload) before the workload allocates.  Where
+    the workload's buffers land in HBM changed the write-heavy AdamW pass by
+    up to 20 % on MI355X (the reduce by about 2 %): allocated first in a
+    fresh process it ran slowest; allocated after such a scratch it ran
+    fastest, for every workload size measured.  Recycling all free memory
+    instead was slow again.  Returns the scratch size in bytes."""
     import torch
     free, _ = torch.cuda.mem_get_info(dev)
-    size = min(int(nbytes * 1.1) + (1 << 30), free - (4 << 30))
+    size = min(max(150 << 30, int(nbytes * 1.1)), free - (8 << 30))
     if size <= 0:
         return 0
     x = torch.empty(size, dtype=torch.uint8, device=dev)
