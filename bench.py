@@ -181,6 +181,18 @@ def copy_calibration():
           flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, sample, steps, threads=1):
     """The CPU oracle on the first `sample` elements of the workload's shard
     (inputs generated beforehand): single-threaded as it stands, or with
@@ -245,7 +257,7 @@ def cpu_baseline(w, sample, steps, threads=1):
             "sample": f"first {sample} elements of the {w.name} shard, {steps} steps, "
                       f"inputs pre-generated, "
                       + ("single thread" if threads == 1 else f"{threads} threads"),
-            "seconds": round(dt, 3), "cpu": platform.processor() or platform.machine(),
+            "seconds": round(dt, 3), "cpu": cpu_model(),
             "host_cpus": os.cpu_count()}
 
 
