@@ -363,10 +363,11 @@ def recycle_device_memory(dev, nbytes):
     """Untimed set-up: write and release a scratch allocation of
     max(150 GiB, 1.1 x the workload) before the workload allocates.  Where
     the workload's buffers land in HBM changed the write-heavy AdamW pass by
-    up to 20 % on MI355X (the reduce by about 2 %): allocated first in a
-    fresh process it ran slowest; allocated after such a scratch it ran
-    fastest, for every workload size measured.  Recycling all free memory
-    instead was slow again.  Returns the scratch size in bytes."""
+    up to 20 % on MI355X (the reduce by about 2 %).  Allocated first in a
+    fresh process, the 30B and 1.3B workloads ran at their slowest; after
+    such a scratch they ran at their fastest in every run measured (the 7B
+    working set varied either way).  Recycling all free memory instead was
+    slow again.  Returns the scratch size in bytes."""
     import torch
     free, _ = torch.cuda.mem_get_info(dev)
     size = min(max(150 << 30, int(nbytes * 1.1)), free - (8 << 30))
