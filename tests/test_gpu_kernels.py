@@ -167,7 +167,7 @@ def test_mx_reduce_decodes_every_code_under_every_scale(zs):
     assert zs.read_norm_acc(acc)[0] == acc_from_oracle(O.norm_accumulate(want))
 
 
-@pytest.mark.parametrize("P", [1, 3, 8])
+@pytest.mark.parametrize("P", [1, 3, 4, 8])
 def test_mx_reduce_and_norm(zs, P):
     """Replicas packed to MXFP8 by the oracle (with inf/NaN blocks, all-zero
     blocks and tiny blocks) against decode-then-reduce in the oracle."""
