@@ -277,26 +277,22 @@ __device__ __forceinline__ double quad_group_sum(double a) {
   return b + dpp_quad_perm(b, 2);
 }
 
-// floor(S * 2^128) split into three 32-bit pieces at digits base, base+1,
-// base+2 (S >= 0 finite, S < 2^64).  Lane q of the quad (0..2) returns
-// piece q and its digit; lane 3 returns 0.
-__device__ __forceinline__ void fixed_point_piece(double S, int quad_lane, int& digit,
-                                                  uint64_t& piece) {
+// floor(S * 2^128) split into three 32-bit pieces p0, p1, p2 at digits
+// base, base+1, base+2 (base + 2 <= 6).  S >= 0; a zero or subnormal S
+// (below 2^-1022, so below one unit) or one >= 2^64 gives three zero pieces.
+__device__ __forceinline__ void fixed_point_split(double S, int& base, uint32_t& p0,
+                                                  uint32_t& p1, uint32_t& p2) {
   const uint64_t bits = __double_as_longlong(S);
   const int ex = static_cast<int>((bits >> 52) & 0x7FF);
-  piece = 0;
-  digit = 0;
-  if (ex == 0 || ex >= 1087) return;  // zero/subnormal (< 2^-1022) or >= 2^64
+  base = 0;
+  p0 = p1 = p2 = 0u;
+  if (ex == 0 || ex >= 1087) return;
   const uint64_t mant = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
   const int sh = ex - 947;  // S * 2^128 = mant * 2^sh
-  uint32_t p0, p1, p2;
-  int base;
   if (sh < 0) {
     const uint64_t v = (sh <= -53) ? 0ull : (mant >> (-sh));
     p0 = static_cast<uint32_t>(v);
     p1 = static_cast<uint32_t>(v >> 32);
-    p2 = 0u;
-    base = 0;
   } else {
     const int r = sh & 31;
     base = sh >> 5;
@@ -306,8 +302,16 @@ __device__ __forceinline__ void fixed_point_piece(double S, int quad_lane, int& 
     p1 = static_cast<uint32_t>(lo >> 32);
     p2 = static_cast<uint32_t>(hi);
   }
-  const uint32_t mine = quad_lane == 0 ? p0 : (quad_lane == 1 ? p1 : (quad_lane == 2 ? p2 : 0u));
-  piece = mine;
+}
+
+// One piece of floor(S * 2^128) per quad lane: lane q (0..2) returns piece q
+// and its digit; lane 3 returns 0.
+__device__ __forceinline__ void fixed_point_piece(double S, int quad_lane, int& digit,
+                                                  uint64_t& piece) {
+  int base;
+  uint32_t p0, p1, p2;
+  fixed_point_split(S, base, p0, p1, p2);
+  piece = quad_lane == 0 ? p0 : (quad_lane == 1 ? p1 : (quad_lane == 2 ? p2 : 0u));
   digit = base + (quad_lane < 3 ? quad_lane : 0);
 }
 

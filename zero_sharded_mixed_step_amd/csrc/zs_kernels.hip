@@ -142,6 +142,23 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
     fixed_point_piece(S, quad_lane, d, piece);
     if (piece != 0) s_digit[d][tid] += piece;  // lane-private row
   };
+  // Norm state of four chunks per lane: every quad lane holds the four
+  // group sums, and lane q converts group q whole (three pieces), so the
+  // fixed-point work is done once per group instead of once per lane.
+  double s4[4];
+  auto norm_chunk4 = [&](int u, const float g[kVec]) {
+    s4[u & 3] = quad_group_sum(chunk_sumsq(g, nonfinite));
+    if ((u & 3) != 3) return;
+    const double S = quad_lane == 0 ? s4[0] : (quad_lane == 1 ? s4[1]
+                                            : (quad_lane == 2 ? s4[2] : s4[3]));
+    if (S >= 18446744073709551616.0) ++overflow;
+    int base;
+    uint32_t p0, p1, p2;
+    fixed_point_split(S, base, p0, p1, p2);
+    if (p0 != 0) s_digit[base][tid] += p0;
+    if (p1 != 0) s_digit[base + 1][tid] += p1;
+    if (p2 != 0) s_digit[base + 2][tid] += p2;
+  };
   // Chunks per lane per fast-path iteration.  PIPE (4 or 8 replicas, launches
   // of up to ZS_REDUCE_PIPE_MAX_ELEMS elements) software-pipelines the fast
   // path: the loads of the next U tiles are in flight while the current U
@@ -178,7 +195,8 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
         float g[kVec];
         sum_raw<DT, PT>(cur[u], prm.inv_scale, g);
         if (WRITE) store_g_tile(prm.g_out, (tile + u) * kThreads + tid, g);
-        if constexpr (NORM) norm_chunk(g);
+        if constexpr (NORM && U % 4 == 0) norm_chunk4(u, g);
+        else if constexpr (NORM) norm_chunk(g);
       }
       if (more) {
 #pragma unroll
@@ -197,7 +215,8 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
           float g[kVec];
           sum_raw<DT, PT>(raw[u], prm.inv_scale, g);
           if (WRITE) store_g_tile(prm.g_out, (tile + u) * kThreads + tid, g);
-          if constexpr (NORM) norm_chunk(g);
+          if constexpr (NORM && U % 4 == 0) norm_chunk4(u, g);
+          else if constexpr (NORM) norm_chunk(g);
         }
       } else {
 #pragma unroll
