@@ -1,0 +1,104 @@
+"""Host-side logic of bench.py, no GPU: the fused-minimum byte accounting of
+every workload and pass structure, the unfused chain's bytes, the scaling of
+rocprofv3 FETCH_SIZE/WRITE_SIZE counters into HBM bytes, and the refusal of a
+multi-GPU run."""
+import csv
+import json
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import pytest
+
+import bench
+from synth import configs
+
+MX = 1 + 1 / 32
+
+
+@pytest.mark.parametrize("name,path,fuse,want", [
+    # 8 bf16 replicas, materialised g: reduce 8*2 + 4, AdamW 4 + 24 + 2 (+ MXFP8)
+    ("30b-shard-p8", "materialize", True, {"reduce": 20, "adamw": 30 + MX}),
+    ("30b-shard-p8", "materialize", False, {"reduce": 20, "adamw": 30, "mxfp8_pack": 2 + MX}),
+    ("7b-shard-p8", "materialize", False, {"reduce": 20, "adamw": 30}),
+    ("gpt2-small-p8", "materialize", False, {"reduce": 20, "adamw": 30}),
+    # one bf16 replica, recomputed: norm pass 2, AdamW 2 + 26
+    ("1.3b-unsharded", "recompute", False, {"reduce": 2, "adamw": 28}),
+    # ungated: one pass, 4 fp32 replicas + 26
+    ("flat-1m-p4", "fused", False, {"adamw": 42}),
+    # MXFP8-stored replicas: 8 * (1 + 1/32) + 4
+    ("30b-shard-p8-mxgrads", "materialize", True, {"reduce": 8 * MX + 4, "adamw": 30 + MX}),
+])
+def test_fused_minimum_bytes(name, path, fuse, want):
+    w = configs.ALL[name]
+    got = bench.per_elem_bytes(w, SimpleNamespace(path=path, fuse_pack=fuse))
+    assert got.keys() == want.keys()
+    for k in want:
+        assert got[k] == pytest.approx(want[k], abs=0), (k, got[k], want[k])
+
+
+def test_step_minimum_matches_the_pass_structure():
+    # gated at P = 8 bf16: min(P*2 + 34, 2*P*2 + 26) = 50; the 30B case adds
+    # the fused MXFP8 output
+    w = configs.SHARD_30B
+    kinds = bench.per_elem_bytes(w, SimpleNamespace(path="materialize", fuse_pack=True))
+    assert sum(kinds.values()) == 50 + MX
+    P, g_b = w.P, w.g_bytes
+    assert min(P * g_b + 34, 2 * P * g_b + 26) == 50
+
+
+def test_unfused_chain_bytes():
+    # sum (P*2 + 4), scale (8), norm (4), clip (8), m (12), v (12),
+    # direction (12), weight (12), cast (6), pack (2 + 1.03125)
+    assert bench.unfused_bytes(configs.SHARD_7B) == 94
+    assert bench.unfused_bytes(configs.SHARD_30B) == 94 + 2 + MX
+
+
+def test_workload_bytes():
+    w = configs.SHARD_30B
+    assert bench.workload_bytes(w) == int(w.S * (8 * 2 + 18 + MX))
+
+
+def _write_counters(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, value in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": "X", "Counter_Value": value})
+
+
+def test_counter_scaling(tmp_path, monkeypatch):
+    """HBM bytes = 1024 * (FETCH_SIZE * f + WRITE_SIZE * w), where the plain
+    1 GiB copy fixes f and w, averaged over dispatches per launch kind."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    copy = "__amd_rocclr_copyBuffer"
+    adamw = "void zs::adamw_kernel<-1, 1, true, true>(zs::AdamParams)"
+    red = "void zs::shard_reduce_kernel<1, 8, true, true, false>(zs::ReduceParams)"
+    d = {k: str(tmp_path / k) for k in ("f", "w", "cf", "cw")}
+    _write_counters(d["cf"], [(copy, 524288.0)])          # a copy reads half its bytes
+    _write_counters(d["cw"], [(copy, 1048576.0)])
+    _write_counters(d["f"], [(adamw, 1000.0), (adamw, 1002.0), (red, 10.0)])
+    _write_counters(d["w"], [(adamw, 700.0), (adamw, 700.0), (red, 5.0)])
+    w = configs.SHARD_30B
+    bench.summarize_pmc(w, [d["f"], d["w"], d["cf"], d["cw"]], "test")
+    rec = json.load(open(tmp_path / "traffic.json"))[w.name]
+    assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    assert rec["source_digest"] == bench.source_digest()
+    assert rec["kinds"]["adamw"] == {"dispatches": 2, "fetch_kib": 1001.0, "write_kib": 700.0,
+                                     "hbm_bytes": 1024 * (1001 * 2 + 700)}
+    assert rec["kinds"]["reduce"]["hbm_bytes"] == 1024 * (10 * 2 + 5)
+    assert "mxfp8_pack" not in rec["kinds"]
+
+
+def test_source_digest_is_stable():
+    a, b = bench.source_digest(), bench.source_digest()
+    assert a == b and len(a) == 16 and int(a, 16) >= 0
+
+
+def test_multi_gpu_run_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
