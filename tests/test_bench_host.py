@@ -1,7 +1,7 @@
-"""Host-side logic of bench.py, no GPU: the fused-minimum byte accounting of
-every workload and pass structure, the unfused chain's bytes, the scaling of
-rocprofv3 FETCH_SIZE/WRITE_SIZE counters into HBM bytes, and the refusal of a
-multi-GPU run."""
+"""Host-side logic, no GPU: the fused-minimum byte accounting of every
+workload and pass structure, the unfused chain's bytes, the scaling of
+rocprofv3 FETCH_SIZE/WRITE_SIZE counters into HBM bytes, the refusal of a
+multi-GPU run (bench.py), and ShardStep's choice of pass structure."""
 import csv
 import json
 import os
@@ -102,3 +102,23 @@ def test_multi_gpu_run_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_pass_structure_choice():
+    """Gated steps materialise g when that moves fewer bytes than re-reducing
+    the replicas (P*g_b + 34 < 2*P*g_b + 26, i.e. P*g_b > 8)."""
+    from zero_sharded_mixed_step_amd import choose_path
+    assert choose_path(4, 4, gated=False) == "fused"
+    assert choose_path(8, 2, gated=True) == "materialize"       # 50 < 58
+    assert choose_path(1, 2, gated=True) == "recompute"         # 30 < 36
+    assert choose_path(4, 2, gated=True) == "recompute"         # 8: tie -> recompute
+    assert choose_path(3, 4, gated=True) == "materialize"       # 46 < 50
+    assert choose_path(1, 2, gated=True, mx_grads=True) == "materialize"
+    for P, g_b in ((1, 2), (2, 2), (4, 2), (8, 2), (1, 4), (3, 4), (8, 4)):
+        mat, rec = P * g_b + 34, 2 * P * g_b + 26
+        got = choose_path(P, g_b, gated=True)
+        assert (got == "materialize") == (mat < rec), (P, g_b, got)
+    with pytest.raises(ValueError):
+        choose_path(8, 2, gated=True, path="fused")
+    with pytest.raises(ValueError):
+        choose_path(8, 2, gated=True, mx_grads=True, path="recompute")

@@ -12,4 +12,4 @@ from ._binding import (ZERO_BF16, ZERO_F32, ZERO_MAX_REPLICAS, ZERO_MXFP8, ZeroS
                        zero_norm_acc_clear, zero_shard_reduce, zero_shard_reduce_mx,
                        zero_step_gate, zero_strerror,
                        zero_unfused_workspace_bytes)
-from .step import ShardStep  # noqa: F401
+from .step import ShardStep, choose_path  # noqa: F401

@@ -37,6 +37,29 @@ import torch
 from . import _binding as B
 
 
+def choose_path(P: int, g_b: float, gated: bool, mx_grads: bool = False,
+                path: Optional[str] = None) -> str:
+    """The pass structure of a step: "fused" (one pass, ungated),
+    "materialize" (reduce writes fp32 g, AdamW re-reads it: P*g_b + 34 B per
+    element) or "recompute" (norm-only pass, then AdamW reduces the replicas
+    again: 2*P*g_b + 26 B), whichever moves fewer bytes when gated.
+    MXFP8-stored replicas are read by the reduce pass only, so they always
+    materialise.  `path` forces a choice (checked)."""
+    if mx_grads:
+        if path not in (None, "materialize"):
+            raise ValueError("MXFP8 gradient replicas need the materialise path")
+        return "materialize"
+    if path is None:
+        if not gated:
+            return "fused"
+        return "materialize" if P * g_b > 8 else "recompute"
+    if path not in ("fused", "materialize", "recompute"):
+        raise ValueError(path)
+    if path == "fused" and gated:
+        raise ValueError("a gated step needs the norm before the update")
+    return path
+
+
 class ShardStep:
     def __init__(self, n: int, P: int, grad_dtype: torch.dtype, *, lr: float,
                  beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
@@ -57,22 +80,9 @@ class ShardStep:
         # gradient is always materialised)
         self.mx_grads = grad_dtype == "mxfp8"
         g_b = 4 if grad_dtype == torch.float32 else 2
-        if self.mx_grads:
-            if path not in (None, "materialize"):
-                raise ValueError("MXFP8 gradient replicas need the materialise path")
-            if self.n % 32:
-                raise ValueError("MXFP8 gradients need n % 32 == 0")
-            path = "materialize"
-        if path is None:
-            if not self.gated:
-                path = "fused"
-            else:
-                path = "materialize" if self.P * g_b > 8 else "recompute"
-        if path not in ("fused", "materialize", "recompute"):
-            raise ValueError(path)
-        if path == "fused" and self.gated:
-            raise ValueError("a gated step needs the norm before the update")
-        self.path = path
+        if self.mx_grads and self.n % 32:
+            raise ValueError("MXFP8 gradients need n % 32 == 0")
+        self.path = path = choose_path(self.P, g_b, self.gated, self.mx_grads, path)
         dev = torch.device(device)
         self.master = torch.empty(self.n, dtype=torch.float32, device=dev)
         self.m = torch.zeros(self.n, dtype=torch.float32, device=dev)
