@@ -737,3 +737,30 @@ def test_graph_replay_matches_eager(zs):
         assert _same_state(eager, graphed), call
         assert eager.applied_steps() == graphed.applied_steps()
     assert graphed.applied_steps() == 6
+
+
+def test_counter_moves_between_host_and_device(zs):
+    """Steps with the count moved device -> host -> device in between (as the
+    benchmark does around the unfused chain) equal host-counted steps, the
+    unfused steps included."""
+    import torch
+    n, P = 4096 + 96, 8
+    ref = zs.ShardStep(n, P, torch.bfloat16, **_HP)
+    mix = zs.ShardStep(n, P, torch.bfloat16, device_counter=True, **_HP)
+    _init(ref, mix)
+    reps = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(P)]
+    for call in range(1, 9):
+        _fill_grads(reps, call, inject_call=3)
+        if call == 4:
+            mix.set_counter(device=False)
+        if call == 6:
+            mix.set_counter(device=True)
+        if 4 <= call < 6:
+            ref.step_unfused(reps)
+            mix.step_unfused(reps)
+        else:
+            ref.step(reps)
+            mix.step(reps)
+        torch.cuda.synchronize()
+        assert _same_state(ref, mix), call
+    assert ref.applied_steps() == mix.applied_steps() == 7
