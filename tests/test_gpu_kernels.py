@@ -649,6 +649,14 @@ def test_zero_length_calls_touch_nothing(zs):
                            param_bf16=param, n=0)
         torch.cuda.synchronize()
         assert int(skipped.item()) == want_skip, (check, want_skip)
+    # the device step counter advances on a zero-length call unless skipped
+    t_dev = torch.full((1,), 41, dtype=torch.int64, device="cuda")
+    for accs, check, want_t in ((bad, True, 41), (acc, True, 42), (bad, False, 43), (None, False, 44)):
+        zs.zero_adamw_step(master, m, v, lr=1e-3, weight_decay=0.01, grad_f32=g,
+                           param_bf16=param, accs=accs, max_norm=1.0, check_overflow=check,
+                           step_dev=t_dev, n=0)
+        torch.cuda.synchronize()
+        assert int(t_dev.item()) == want_t, (check, want_t)
     assert torch.all(master == 0.25).item() and torch.all(m == 0.5).item()
     assert torch.all(v == 0.75).item() and torch.all(param == 0x1234).item()
     assert torch.all(elem == 0xAB).item() and torch.all(scale == 0xCD).item()
