@@ -65,6 +65,10 @@ def parse():
                          "scratch allocation of its size")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused single-operation chain")
+    ap.add_argument("--placement-probe", type=float, default=None, metavar="GB",
+                    help="only time the step's reduce and AdamW launches in two placements: "
+                         "the workload allocated first, then again after a held, written "
+                         "spacer allocation of GB gigabytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM "
                          "byte counters)")
@@ -381,6 +385,52 @@ def recycle_device_memory(dev, nbytes):
     return size
 
 
+def placement_probe(w, spacer_gb):
+    """Time the step's reduce and AdamW launches with the workload's buffers
+    allocated first in the process, then again after a held, written spacer
+    allocation: the same kernels and inputs in two placements in HBM."""
+    import torch
+
+    import synth
+    import zero_sharded_mixed_step_amd as zs
+    dev = torch.device("cuda:0")
+    spacers = []
+    for phase, spacer in (("first", 0.0), ("after spacer", spacer_gb)):
+        while sum(x.numel() for x in spacers) < spacer * 1e9:
+            x = torch.empty(min(5 * 10**9, int(spacer * 1e9) - sum(y.numel() for y in spacers)),
+                            dtype=torch.uint8, device=dev)
+            x.fill_(1)
+            spacers.append(x)
+        st = zs.ShardStep(w.S, w.P, torch.bfloat16 if w.grad_bf16 else torch.float32, lr=w.lr,
+                          beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
+                          max_norm=w.max_norm, check_overflow=w.check_overflow,
+                          loss_scale=w.loss_scale, bucket=w.bucket, pack=w.pack,
+                          device_counter=True, device=dev)
+        synth.fill_device(w.master_spec(), w.shard_start(), st.master)
+        synth.fill_device(w.master_spec(), w.shard_start(), st.param)
+        reps = []
+        for k in range(w.P):
+            r = torch.empty(w.S, dtype=torch.int16 if w.grad_bf16 else torch.float32, device=dev)
+            synth.fill_device(w.grad_spec(1, k), w.shard_start(), r)
+            reps.append(r)
+        times = []
+        for _ in range(3):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record()
+            st.reduce(reps)
+            b.record()
+            st.update(reps)
+            c.record()
+            torch.cuda.synchronize()
+            times.append({"reduce_ms": round(a.elapsed_time(b), 3),
+                          "adamw_ms": round(b.elapsed_time(c), 3)})
+        print(json.dumps({"workload": w.name, "placement": phase, "spacer_gb": spacer,
+                          "steps": times}), flush=True)
+        del st, reps
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -398,6 +448,11 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.placement_probe is not None:
+        from synth import configs
+        placement_probe(configs.ALL[args.config], args.placement_probe)
         return
 
     import synth
