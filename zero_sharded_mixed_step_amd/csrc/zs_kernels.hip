@@ -608,7 +608,7 @@ hipError_t launch_acc_clear(zero_norm_acc* accs, int n_accs, hipStream_t stream)
 // -------------------------------------------------------------- MXFP8 ----
 
 #ifndef ZS_MX_UNROLL
-#define ZS_MX_UNROLL 4
+#define ZS_MX_UNROLL 8
 #endif
 
 // ZS_MX_UNROLL tiles per iteration, so that several 16-byte loads per lane
