@@ -721,30 +721,53 @@ def test_device_counter_matches_host_counter(zs):
     assert host.applied_steps() == dev.applied_steps() == 100_000
 
 
-def test_graph_replay_matches_eager(zs):
-    """One step (35-odd bucketed reduce launches, gated AdamW, fused MXFP8)
-    recorded once and replayed: after every replay, with eager work and
-    synchronisation between replays, the state is bitwise that of the same
-    step run eagerly, including a skipped replay."""
+@pytest.mark.parametrize("case", ["buckets", "recompute", "fused"])
+def test_graph_replay_matches_eager(zs, case):
+    """One step recorded once and replayed: after every replay, with eager
+    work and synchronisation between replays, the state is bitwise that of
+    the same step run eagerly.  Cases: 8 bf16 replicas in 34 buckets with the
+    gate and fused MXFP8 (materialised g, a skipped replay); one bf16 replica
+    with a loss scale and the overflow check (recompute path, a skipped
+    replay); 4 fp32 replicas, no gate (one fused pass)."""
     import torch
-    n, P = 65536 + 96, 8
-    eager = zs.ShardStep(n, P, torch.bfloat16, device_counter=True, bucket=32 * 61, **_HP)
-    graphed = zs.ShardStep(n, P, torch.bfloat16, device_counter=True, bucket=32 * 61, **_HP)
+    n = 65536 + 96
+    if case == "buckets":
+        P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, bucket=32 * 61), 4
+    elif case == "recompute":
+        P, dt, skip_call = 1, torch.bfloat16, 4
+        kw = dict(lr=1e-3, weight_decay=0.01, check_overflow=True, loss_scale=65536.0, pack=True)
+    else:
+        P, dt, skip_call = 4, torch.float32, 0
+        kw = dict(lr=1e-3, weight_decay=0.01, pack=True)
+    eager = zs.ShardStep(n, P, dt, device_counter=True, **kw)
+    graphed = zs.ShardStep(n, P, dt, device_counter=True, **kw)
+    assert eager.path == {"buckets": "materialize", "recompute": "recompute",
+                          "fused": "fused"}[case]
     _init(eager, graphed)
-    reps = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(P)]
-    _fill_grads(reps, 1, inject_call=0)
+    reps = [torch.empty(n, dtype=torch.int16 if dt == torch.bfloat16 else torch.float32,
+                        device="cuda") for _ in range(P)]
+
+    def fill(call):
+        for k, r in enumerate(reps):
+            synth.fill_device(synth.make_spec(seed=4, cfg=61, stream=1, step=call, replica=k,
+                                              sigma=1e-3, post_mul=kw.get("loss_scale", 1.0)),
+                              0, r)
+        if call == skip_call:
+            reps[P - 1][77] = 0x7F80 if dt == torch.bfloat16 else float("inf")
+
+    fill(1)
     torch.cuda.synchronize()
     g = graphed.capture(reps)                  # records; runs nothing
     torch.cuda.synchronize()
     assert graphed.applied_steps() == 0 and _same_state(eager, graphed)
     for call in range(1, 8):
-        _fill_grads(reps, call, inject_call=4)
+        fill(call)
         eager.step(reps)
         g.replay()
         torch.cuda.synchronize()
         assert _same_state(eager, graphed), call
         assert eager.applied_steps() == graphed.applied_steps()
-    assert graphed.applied_steps() == 6
+    assert graphed.applied_steps() == (6 if skip_call else 7)
 
 
 def test_counter_moves_between_host_and_device(zs):
