@@ -65,6 +65,16 @@ def parse():
                          "scratch allocation of its size")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused single-operation chain")
+    ap.add_argument("--trace-report", nargs=2, metavar=("PROF_DIR", "BENCH_LOG"),
+                    help="no GPU: print the text summary of a rocprofv3 --kernel-trace --stats "
+                         "run of this workload (PROF_DIR) and the bench line it printed "
+                         "(BENCH_LOG)")
+    ap.add_argument("--traffic-report", nargs="+", metavar="WORKLOAD",
+                    help="no GPU: print the HBM-traffic table of these workloads from "
+                         "profiles/hbm_traffic.json")
+    ap.add_argument("--placement-report", nargs="+", metavar="PROF_DIR_AND_LOG",
+                    help="no GPU: print the per-launch counters of --placement-probe runs, "
+                         "given as pairs: rocprofv3 --pmc output dir, log of that run")
     ap.add_argument("--placement-probe", type=float, default=None, metavar="GB",
                     help="only time the step's reduce and AdamW launches in two placements: "
                          "the workload allocated first, then again after a held, written "
@@ -163,6 +173,196 @@ def summarize_pmc(w, dirs, cmdline):
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(data, fh, indent=1, sort_keys=True)
     print(json.dumps(data[w.name]))
+
+
+def _path_of(w):
+    """The pass structure ShardStep picks for the workload (pure function)."""
+    sys.path.insert(0, ROOT)
+    from zero_sharded_mixed_step_amd.step import choose_path
+    return choose_path(w.P, MX_BYTES if w.mx_grads else w.g_bytes, w.gated, w.mx_grads)
+
+
+def algorithmic_bytes_per_launch(w, kind):
+    """Fused-minimum bytes of one launch of `kind`: bytes per element times
+    the elements one launch covers (a bucket for the bucketed reduce)."""
+    from types import SimpleNamespace
+    per = per_elem_bytes(w, SimpleNamespace(path=_path_of(w), fuse_pack=w.pack))
+    if kind == "mxfp8_pack":
+        return (2 + MX_BYTES) * w.S
+    elems = w.bucket if (kind == "reduce" and w.bucket) else w.S
+    return per[kind] * elems
+
+
+def step_kernels(w):
+    """(rocprofv3 kernel name, role, launches per step) of the kernels one
+    step of the workload launches, from the pass structure and the library's
+    dispatch: reduce template <replica dtype, P, writes g, norm, pipelined>
+    (pipelined for P >= 4 and at most 2^27 elements a launch), AdamW template
+    <gradient source (-1: materialised g), P, bf16 param, fused MXFP8>."""
+    path = _path_of(w)
+    dt = 2 if w.mx_grads else (1 if w.grad_bf16 else 0)
+    pt = w.P if w.P in (1, 2, 4, 8) else 0
+    per_launch = w.bucket or w.S
+    pipe = "true" if (pt >= 4 and per_launch <= (1 << 27)) else "false"
+    launches = -(-w.S // w.bucket) if w.bucket else 1
+    mx = "true" if w.pack else "false"
+    out = []
+    if path == "materialize":
+        out.append((f"void zs::shard_reduce_kernel<{dt}, {pt}, true, true, {pipe}>"
+                    "(zs::ReduceParams)", "reduce + norm, writes fp32 g", launches))
+        out.append((f"void zs::adamw_kernel<-1, 1, true, {mx}>(zs::AdamParams)",
+                    "gated AdamW reading g" + (", fused MXFP8" if w.pack else ""), 1))
+    elif path == "recompute":
+        out.append((f"void zs::shard_reduce_kernel<{dt}, {pt}, false, true, {pipe}>"
+                    "(zs::ReduceParams)", "norm-only pass over the replicas", launches))
+        out.append((f"void zs::adamw_kernel<{dt}, {pt}, true, {mx}>(zs::AdamParams)",
+                    "gated AdamW reducing the replicas again"
+                    + (", fused MXFP8" if w.pack else ""), 1))
+    else:
+        out.append((f"void zs::adamw_kernel<{dt}, {pt}, true, {mx}>(zs::AdamParams)",
+                    "one pass: reduce + AdamW" + (", fused MXFP8" if w.pack else ""), 1))
+    out.append(("zs::step_advance_kernel(long*, zero_norm_acc const*, int, double, int)",
+                "device step counter", 1))
+    return out
+
+
+PROFILE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_<TAG> "
+               "-o run -- python3 $R/bench.py --config {cfg} --steps 5 --warmup 1 "
+               "--no-cpu-baseline")
+
+
+def trace_report(w, prof_dir, bench_log):
+    """Text summary of a kernel-trace run: rocprofv3's per-kernel statistics
+    and the bench line the same run printed."""
+    import csv
+    cols = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+            "StdDev"]
+    with open(os.path.join(prof_dir, "run_kernel_stats.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    line = next((ln.strip() for ln in open(bench_log) if ln.startswith("{")), None)
+    print(f"# rocprofv3 kernel-trace summary: optimizer step, {w.name} ({w.title})")
+    print("# MI355X (gfx950), one GPU.  Data (run from /tmp with TMPDIR=/tmp, repo at $R):")
+    print("#   " + PROFILE_CMD.format(cfg=w.name))
+    print(f"# This summary: python bench.py --trace-report <prof dir> <log of that run> "
+          f"--config {w.name}")
+    print(f"# Pass structure: {_path_of(w)}; bucket: {w.bucket}.  Durations in ns.  The run "
+          "also times the unfused chain (unfused_kernel<..>, gate_kernel, and")
+    print("# shard_reduce_kernel / mxfp8_kernel launches of the chain); fill_kernel is the "
+          "input generator and FillFunctor torch fills (set-up, untimed).")
+    print(f"# Kernel sources digest (bench.py source_digest): {source_digest()}")
+    print("# Kernels of one step (role, launches per step, average ns from the table):")
+    avg = {r["Name"]: float(r["AverageNs"]) for r in rows}
+    for name, role, launches in step_kernels(w):
+        key = name if name in avg else None
+        got = f"{avg[key]:.0f} ns" if key else "NOT IN THE TABLE"
+        print(f"#   {name.split('(')[0]}: {role}; {launches}/step; {got}")
+    print("#")
+    print(",".join(f'"{c}"' for c in cols))
+    for r in rows:
+        print(",".join([f'"{r["Name"]}"'] + [r[c] for c in cols[1:]]))
+    print("#")
+    print("# bench.py line printed by the same run (roofline.traffic is null there when the "
+          "counters of these kernels were summarised after it):")
+    print(line)
+
+
+def traffic_report(names):
+    """Text table of the HBM traffic per launch stored in hbm_traffic.json,
+    against the algorithmic bytes of the same launch."""
+    from synth import configs
+    with open(TRAFFIC_FILE) as fh:
+        data = json.load(fh)
+    digests = sorted({data[n]["source_digest"] for n in names})
+    print("# HBM traffic per launch from rocprofv3 counters: " + ", ".join(names))
+    print(f"# MI355X (gfx950), one GPU.  Kernel sources digest: {', '.join(digests)}")
+    print("# Counter runs (each its own process, from /tmp with TMPDIR=/tmp, repo at $R), "
+          "for CTR in FETCH_SIZE WRITE_SIZE:")
+    print("#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/pmc_copy_$CTR -o run "
+          "-- python3 $R/bench.py --copy-calibration")
+    print("#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/pmc_<TAG>_$CTR -o run "
+          "-- python3 $R/bench.py --config <WORKLOAD> --steps 2 --warmup 1 --no-cpu-baseline "
+          "--no-unfused")
+    print("# Scaled (no GPU): python bench.py --summarize-pmc pmc_<TAG>_FETCH_SIZE "
+          "pmc_<TAG>_WRITE_SIZE pmc_copy_FETCH_SIZE pmc_copy_WRITE_SIZE --config <WORKLOAD>")
+    print("#   -> profiles/hbm_traffic.json; this table: python bench.py --traffic-report "
+          + " ".join(names))
+    print("# HBM bytes = 1024 * (FETCH_SIZE * f + WRITE_SIZE * w); a plain 1 GiB copy reads "
+          "FETCH_SIZE = 1 GiB / f and WRITE_SIZE = 1 GiB / w (in KiB), so:")
+    for n in names:
+        print(f"#   {n}: f = {data[n]['fetch_factor']:.4f}, w = {data[n]['write_factor']:.4f}")
+    print("#")
+    print(f"# {'workload':22s} {'kind':11s} {'dispatches':>10s} {'FETCH_SIZE KiB':>15s} "
+          f"{'WRITE_SIZE KiB':>15s} {'HBM bytes/launch':>17s} {'algorithmic':>15s}  ratio")
+    for n in names:
+        w = configs.ALL[n]
+        for kind, k in sorted(data[n]["kinds"].items()):
+            alg = algorithmic_bytes_per_launch(w, kind)
+            print(f"  {n:22s} {kind:11s} {k['dispatches']:10d} {k['fetch_kib']:15.1f} "
+                  f"{k['write_kib']:15.1f} {k['hbm_bytes']:17d} {alg:15.0f}  "
+                  f"{k['hbm_bytes'] / alg:.4f}")
+    print("#")
+    print("# reduce = shard_reduce_kernel (replicas -> fp32 g and norm state, or the norm "
+          "state alone), adamw = adamw_kernel (master/m/v update, bf16 param, fused MXFP8 "
+          "output where set), mxfp8_pack = mxfp8_kernel (standalone pack, and the set-up "
+          "packing of MXFP8-stored replicas).")
+    print("# Algorithmic bytes per element: reduce P*g_b + 4 (materialised g) or P*g_b (norm "
+          "only); AdamW 30 with g read, P*g_b + 26 when it re-reduces the replicas, +1.03125 "
+          "with the fused MXFP8 output; pack 3.03125.  The bucketed reduce launch covers one "
+          "bucket.")
+
+
+def placement_report(pairs):
+    """Per-launch counters of the reduce and AdamW launches of placement-probe
+    runs (one rocprofv3 --pmc pass each): the first half of the launches
+    uses the buffers allocated first, the second half the same buffers after
+    the spacer.  Also echoes each run's bench line."""
+    import csv
+    if len(pairs) % 2:
+        raise SystemExit("--placement-report takes (dir, log) pairs")
+    runs = [(pairs[i], pairs[i + 1]) for i in range(0, len(pairs), 2)]
+    print("# Per-launch counters of the 30B-shard step's reduce and AdamW launches in two "
+          "placements of the same buffers:")
+    print("# allocated first in the process, then again after a held, written spacer "
+          "(bench.py --placement-probe GB).")
+    print("# MI355X (gfx950), one GPU.  One counter pass per run (its own process, from /tmp "
+          "with TMPDIR=/tmp, repo at $R):")
+    print("#   rocprofv3 --pmc <COUNTERS> --output-format csv -d $R/gpurun_out/<DIR> -o run "
+          "-- python3 $R/bench.py --placement-probe 60")
+    print("# This summary: python bench.py --placement-report " + " ".join(
+        f"<DIR{i}> <LOG{i}>" for i in range(1, len(runs) + 1)))
+    print("# Launch durations (ms) are rocprofv3's per-dispatch timestamps under counter "
+          "collection.  TCC_EA0 DRAM read requests are 128 B, write requests 64 B; GMI = "
+          "inter-die.")
+    logs = []
+    for k, (d, log) in enumerate(runs, 1):
+        with open(os.path.join(d, "run_counter_collection.csv")) as fh:
+            rows = list(csv.DictReader(fh))
+        launches, names = {}, []
+        for r in rows:
+            kn = r["Kernel_Name"]
+            if "adamw_kernel" not in kn and "shard_reduce_kernel" not in kn:
+                continue
+            e = launches.setdefault(int(r["Dispatch_Id"]), {
+                "kind": "adamw" if "adamw_kernel" in kn else "reduce",
+                "ms": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6})
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            e[c] = float(r["Counter_Value"])
+        order = [launches[i] for i in sorted(launches)]
+        print("#")
+        print(f"# pass {k}: " + " ".join(names))
+        print("# placement  kind       ms  " + "  ".join(f"{c:>{max(14, len(c))}s}"
+                                                      for c in names))
+        for i, e in enumerate(order):
+            pl = "first" if i < len(order) // 2 else "spacer"
+            print(f"  {pl:9s}  {e['kind']:6s} {e['ms']:7.2f}  " + "  ".join(
+                f"{e.get(c, float('nan')):>{max(14, len(c))}.0f}" for c in names))
+        logs += [ln.strip() for ln in open(log) if ln.startswith("{")]
+    print("#")
+    print("# bench.py lines of the runs (in-process HIP events per launch):")
+    for ln in logs:
+        print("# " + ln)
 
 
 def copy_calibration():
@@ -442,6 +642,16 @@ def main():
     if args.summarize_pmc:
         from synth import configs
         summarize_pmc(configs.ALL[args.config], args.summarize_pmc, " ".join(sys.argv))
+        return
+    if args.trace_report:
+        from synth import configs
+        trace_report(configs.ALL[args.config], *args.trace_report)
+        return
+    if args.placement_report:
+        placement_report(args.placement_report)
+        return
+    if args.traffic_report:
+        traffic_report(args.traffic_report)
         return
 
     import torch

@@ -122,3 +122,33 @@ def test_pass_structure_choice():
         choose_path(8, 2, gated=True, path="fused")
     with pytest.raises(ValueError):
         choose_path(8, 2, gated=True, mx_grads=True, path="recompute")
+
+
+@pytest.mark.parametrize("name,kernels", [
+    ("30b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, false>(zs::ReduceParams)",
+                      "void zs::adamw_kernel<-1, 1, true, true>(zs::AdamParams)"]),
+    ("7b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, true>(zs::ReduceParams)",
+                     "void zs::adamw_kernel<-1, 1, true, false>(zs::AdamParams)"]),
+    ("1.3b-unsharded", ["void zs::shard_reduce_kernel<1, 1, false, true, false>(zs::ReduceParams)",
+                        "void zs::adamw_kernel<1, 1, true, false>(zs::AdamParams)"]),
+    ("flat-1m-p4", ["void zs::adamw_kernel<0, 4, true, false>(zs::AdamParams)"]),
+])
+def test_step_kernel_names(name, kernels):
+    """The kernels a step launches, named as rocprofv3 prints them, follow the
+    pass structure; the 35 buckets of the 7B shard take one reduce each."""
+    got = bench.step_kernels(configs.ALL[name])
+    assert [k for k, _, _ in got[:-1]] == kernels
+    assert got[-1][0].startswith("zs::step_advance_kernel(")
+    if name == "7b-shard-p8":
+        assert got[0][2] == 35
+
+
+def test_traffic_report_ratios(capsys):
+    """The committed counter table: every launch kind within 3% of its
+    algorithmic bytes (re-reads would show as a larger ratio)."""
+    bench.traffic_report(["30b-shard-p8", "7b-shard-p8"])
+    rows = [ln.split() for ln in capsys.readouterr().out.splitlines()
+            if ln and not ln.startswith("#")]
+    assert len(rows) == 5
+    for r in rows:
+        assert 0.99 < float(r[-1]) < 1.03, r
