@@ -54,7 +54,7 @@ def test_device_generator_matches_host(zs, bf16):
 SIZES = [1, 7, 8, 17, 31, 33, 1024, 4097, 65536 + 13]
 
 
-@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8, 16, 64])   # 64 = ZERO_MAX_REPLICAS
 @pytest.mark.parametrize("bf16", [False, True])
 def test_shard_reduce_and_norm(zs, P, bf16):
     import torch
@@ -167,7 +167,7 @@ def test_mx_reduce_decodes_every_code_under_every_scale(zs):
     assert zs.read_norm_acc(acc)[0] == acc_from_oracle(O.norm_accumulate(want))
 
 
-@pytest.mark.parametrize("P", [1, 3, 4, 8])
+@pytest.mark.parametrize("P", [1, 3, 4, 8, 64])
 def test_mx_reduce_and_norm(zs, P):
     """Replicas packed to MXFP8 by the oracle (with inf/NaN blocks, all-zero
     blocks and tiny blocks) against decode-then-reduce in the oracle."""
@@ -307,7 +307,8 @@ def test_gate_matches_oracle(zs):
 HP = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (0.1, 0.5, 0.75, 1e-3, 0.5)]
 
 
-@pytest.mark.parametrize("source", ["grad_f32", "f32_P4", "bf16_P8", "bf16_P1", "bf16_P3"])
+@pytest.mark.parametrize("source", ["grad_f32", "f32_P4", "bf16_P8", "bf16_P1", "bf16_P3",
+                                    "bf16_P16", "f32_P64"])
 @pytest.mark.parametrize("gated", [False, True])
 def test_adamw_multi_step(zs, source, gated):
     import torch
