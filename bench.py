@@ -240,9 +240,13 @@ def trace_report(w, prof_dir, bench_log):
     with open(os.path.join(prof_dir, "run_kernel_stats.csv")) as fh:
         rows = list(csv.DictReader(fh))
     line = next((ln.strip() for ln in open(bench_log) if ln.startswith("{")), None)
+    cmd = PROFILE_CMD.format(cfg=w.name)
+    if line and "command" in json.loads(line):
+        args = json.loads(line)["command"].split()[2:]
+        cmd = cmd.split(" -- ")[0] + " -- python3 $R/bench.py" + "".join(" " + a for a in args)
     print(f"# rocprofv3 kernel-trace summary: optimizer step, {w.name} ({w.title})")
     print("# MI355X (gfx950), one GPU.  Data (run from /tmp with TMPDIR=/tmp, repo at $R):")
-    print("#   " + PROFILE_CMD.format(cfg=w.name))
+    print("#   " + cmd)
     print(f"# This summary: python bench.py --trace-report <prof dir> <log of that run> "
           f"--config {w.name}")
     print(f"# Pass structure: {_path_of(w)}; bucket: {w.bucket}.  Durations in ns.  The run "
@@ -631,6 +635,14 @@ def placement_probe(w, spacer_gb):
         torch.cuda.empty_cache()
 
 
+_T0 = time.perf_counter()
+
+
+def progress(msg):
+    """One line per finished phase on stderr (stdout carries only the JSON line)."""
+    print(f"bench [{time.perf_counter() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -701,6 +713,7 @@ def main():
             synth.fill_device(w.grad_spec(1, k), start, r)
             reps.append(r)
     torch.cuda.synchronize()
+    progress(f"{w.name}: inputs resident ({w.P} replicas of {w.S} elements)")
 
     kinds = per_elem_bytes(w, st)
     events = {k: [] for k in kinds}
@@ -744,6 +757,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     applied = st.applied_steps()
+    progress(f"{args.warmup} warmup + {args.steps} timed steps done: "
+             f"{1e3 * elapsed / args.steps:.3f} ms/step")
 
     # The standalone MXFP8 pack entry point (outside the timed step: the step
     # packs inside AdamW), timed on its own for its roofline.
@@ -782,6 +797,7 @@ def main():
                    "launches_per_step": 11 + (1 if w.pack else 0),
                    "fused_speedup": round(u_ms / (1e3 * elapsed / args.steps), 3)}
         st.set_counter(device=True)
+        progress(f"unfused chain timed: {u_ms:.3f} ms/step")
 
     # Cold steps for workloads whose step fits in the caches (L2 4 MB per XCD,
     # 256 MB MALL): a 1 GiB scratch write before each step evicts the state,
@@ -895,9 +911,11 @@ def main():
                                      "scaled by a plain-copy calibration)",
                      "traffic_vs_algorithmic": traffic[1] if traffic else None},
         "cpu_baseline": None,
+        "command": " ".join(["python", "bench.py", *sys.argv[1:]]),
     }
     threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline (bounded sample) starts")
         out["cpu_baseline"] = cpu_baseline_leg(w, args, threads, ms_per_step,
                                                kernel_ms.get("reduce"))
     print(json.dumps(out), flush=True)
