@@ -35,9 +35,8 @@
  *     kernels were launched.  Faults inside them surface at the caller's next
  *     synchronisation.
  *   - The caller owns every buffer.  The library allocates nothing, never
- *     synchronises, keeps no state between calls other than caches of each
- *     device's compute-unit count and of each kernel's resident workgroups
- *     per compute unit, and lets no C++ exception escape.
+ *     synchronises, keeps no state between calls other than a cache of each
+ *     device's compute-unit count, and lets no C++ exception escape.
  *   - Device pointers must be 16-byte aligned (ZERO_EALIGN otherwise).
  *     Outputs must not overlap inputs, except master/m/v, which are updated
  *     in place.

@@ -52,23 +52,18 @@ __host__ __device__ inline AdamScalars derive_adam_scalars(const AdamHyper& h, i
   return s;
 }
 
-// Workgroups (of 256 threads) per compute unit of each persistent grid,
-// from sweeps of 1..10 on MI355X: the reduce pass needs 4 to keep enough
+// Workgroups (of 256 threads) per compute unit of the reduce pass's
+// persistent grid, from sweeps of 1..10 on MI355X: it needs 4 to keep enough
 // loads in flight, except for bucket-sized launches with 4 or 8 replicas,
 // whose software-pipelined fast path holds twice the loads per lane and runs
-// best at 1; the pack runs best at 8.  AdamW launches as many as a compute unit holds at once (the
-// occupancy query); ZS_ADAMW_BLOCKS_PER_CU is the fallback.
+// best at 1.  (The reduce stays persistent: each workgroup ends with atomic
+// adds to the one norm accumulator, which a one-shot grid would multiply.
+// AdamW and the pack launch one-shot grids.)
 #ifndef ZS_REDUCE_BLOCKS_PER_CU
 #define ZS_REDUCE_BLOCKS_PER_CU 4
 #endif
 #ifndef ZS_REDUCE_PIPE_BLOCKS_PER_CU
 #define ZS_REDUCE_PIPE_BLOCKS_PER_CU 1
-#endif
-#ifndef ZS_ADAMW_BLOCKS_PER_CU
-#define ZS_ADAMW_BLOCKS_PER_CU 4
-#endif
-#ifndef ZS_PACK_BLOCKS_PER_CU
-#define ZS_PACK_BLOCKS_PER_CU 8
 #endif
 
 int compute_units(int device);

@@ -1,12 +1,11 @@
 // zs_kernels.hip -- the optimizer step's HIP kernels for CDNA4 (gfx950).
 //
 // All four are HBM-bandwidth-bound streaming passes (no matrix work, so no
-// MFMA): 16-byte vector loads/stores per lane, a persistent grid of a few
-// workgroups per compute unit striding over 2048-element tiles, and the norm
-// state reduced in registers (quad DPP), lane-private LDS rows and one set
-// of integer atomics per workgroup.
-#include <atomic>
-
+// MFMA): 16-byte vector loads/stores per lane over 2048-element tiles.  The
+// reduce runs a persistent grid of a few workgroups per compute unit, so its
+// norm state (reduced in registers by quad DPP, then in lane-private LDS
+// rows) meets one set of integer atomics per workgroup; AdamW and the pack
+// run one-shot grids of a few tiles per workgroup.
 #include "zs_device.h"
 #include "zs_internal.h"
 
@@ -37,40 +36,20 @@ static unsigned grid_for(uint64_t nchunks, int blocks_per_cu) {
   return static_cast<unsigned>(g > 0 ? g : 1);
 }
 
-// Workgroups of `kernel` that one compute unit holds at once (set by its
-// register and LDS footprint), from the runtime's occupancy query, cached per
-// kernel; `fallback` if the runtime cannot tell.  A persistent grid of exactly
-// this many workgroups per CU runs in one round: a larger one would run as a
-// full round followed by a partial one.
-static int resident_per_cu(const void* kernel, int fallback) {
-  constexpr int kSlots = 64;
-  static std::atomic<const void*> keys[kSlots];
-  static std::atomic<int> vals[kSlots];
-  int slot = -1;
-  for (int i = 0; i < kSlots; ++i) {
-    const void* k = keys[i].load(std::memory_order_acquire);
-    if (k == kernel) {
-      const int v = vals[i].load(std::memory_order_relaxed);
-      if (v > 0) return v;
-      slot = i;
-      break;
-    }
-    if (k == nullptr) {
-      const void* expected = nullptr;
-      if (keys[i].compare_exchange_strong(expected, kernel) || expected == kernel) {
-        slot = i;
-        break;
-      }
-    }
-  }
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, 0) != hipSuccess ||
-      nb <= 0) {
-    (void)hipGetLastError();  // the query's own failure is not a launch error
-    nb = fallback;
-  }
-  if (slot >= 0) vals[slot].store(nb, std::memory_order_relaxed);
-  return nb;
+// One-shot grid: every workgroup takes U consecutive tiles and exits, so the
+// hardware dispatcher hands out tiles in address order and the stream's
+// front stays compact.  Measured on MI355X, write-heavy streams run faster
+// this way than on a persistent grid that strides over the array: a plain
+// 15 GB write 6.8 vs 5.5-5.8 TB/s, the AdamW pass 2-6 % and the MXFP8 pack
+// 10 % faster, with bitwise the same results.  Grids beyond the dispatch
+// limit (2^32 work-items) are capped; the kernels' grid-stride loops then
+// take the rest.
+static unsigned grid_oneshot(uint64_t nchunks, int u) {
+  const uint64_t ntiles = (nchunks + kThreads - 1) / kThreads;
+  const uint64_t cap = 0xFFFFFFFFull / kThreads;
+  uint64_t g = (ntiles + u - 1) / u;
+  if (g > cap) g = cap;
+  return static_cast<unsigned>(g > 0 ? g : 1);
 }
 
 static Replicas pack_replicas(const void* const* replicas, int P) {
@@ -498,10 +477,9 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
 
 template <int SRC, int PT, bool PARAM, bool MX>
 static void adamw_launch(const AdamParams& prm, hipStream_t st) {
-  const auto kernel = adamw_kernel<SRC, PT, PARAM, MX>;
-  const int per_cu =
-      resident_per_cu(reinterpret_cast<const void*>(kernel), ZS_ADAMW_BLOCKS_PER_CU);
-  hipLaunchKernelGGL(kernel, dim3(grid_for(prm.nchunks, per_cu)), dim3(kThreads), 0, st, prm);
+  hipLaunchKernelGGL((adamw_kernel<SRC, PT, PARAM, MX>),
+                     dim3(grid_oneshot(prm.nchunks, ZS_ADAMW_UNROLL)), dim3(kThreads), 0, st,
+                     prm);
 }
 
 template <int SRC, int PT>
@@ -649,7 +627,7 @@ __global__ void __launch_bounds__(kThreads) mxfp8_kernel(const uint16_t* in, uin
 hipError_t launch_mxfp8(const uint16_t* in, uint64_t n, uint8_t* elem, uint8_t* scale,
                         hipStream_t stream, const Gate* gate) {
   const uint64_t nchunks = n / kVec;
-  const unsigned grid = grid_for(nchunks, ZS_PACK_BLOCKS_PER_CU);
+  const unsigned grid = grid_oneshot(nchunks, ZS_MX_UNROLL);
   hipLaunchKernelGGL(mxfp8_kernel, dim3(grid), dim3(kThreads), 0, stream, in, nchunks, elem,
                      scale, gate);
   return hipGetLastError();
