@@ -196,25 +196,36 @@ def algorithmic_bytes_per_launch(w, kind):
 def step_kernels(w):
     """(rocprofv3 kernel name, role, launches per step) of the kernels one
     step of the workload launches, from the pass structure and the library's
-    dispatch: reduce template <replica dtype, P, writes g, norm, pipelined>
-    (pipelined for P >= 4 and at most 2^27 elements a launch), AdamW template
-    <gradient source (-1: materialised g), P, bf16 param, fused MXFP8>."""
+    dispatch: reduce template <replica dtype, P, writes g, norm, pipelined,
+    one-shot> (one-shot with P >= 4 above 2^27 elements a launch, where
+    ShardStep passes the workspace, then a fold launch; else pipelined for
+    P in {4, 8}), AdamW template <gradient source (-1: materialised g), P,
+    bf16 param, fused MXFP8>."""
+    from zero_sharded_mixed_step_amd.step import ONESHOT_MIN
     path = _path_of(w)
     dt = 2 if w.mx_grads else (1 if w.grad_bf16 else 0)
     pt = w.P if w.P in (1, 2, 4, 8) else 0
     per_launch = w.bucket or w.S
-    pipe = "true" if (pt >= 4 and per_launch <= (1 << 27)) else "false"
+    oneshot = w.P >= 4 and per_launch > ONESHOT_MIN
+    pipe = "true" if (not oneshot and pt >= 4 and per_launch <= (1 << 27)) else "false"
+    form = f"{pipe}, {'true' if oneshot else 'false'}"
     launches = -(-w.S // w.bucket) if w.bucket else 1
     mx = "true" if w.pack else "false"
     out = []
+    fold = ("zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
+            "adds the one-shot reduce's slots to the accumulator", launches)
     if path == "materialize":
-        out.append((f"void zs::shard_reduce_kernel<{dt}, {pt}, true, true, {pipe}>"
+        out.append((f"void zs::shard_reduce_kernel<{dt}, {pt}, true, true, {form}>"
                     "(zs::ReduceParams)", "reduce + norm, writes fp32 g", launches))
+        if oneshot:
+            out.append(fold)
         out.append((f"void zs::adamw_kernel<-1, 1, true, {mx}>(zs::AdamParams)",
                     "gated AdamW reading g" + (", fused MXFP8" if w.pack else ""), 1))
     elif path == "recompute":
-        out.append((f"void zs::shard_reduce_kernel<{dt}, {pt}, false, true, {pipe}>"
+        out.append((f"void zs::shard_reduce_kernel<{dt}, {pt}, false, true, {form}>"
                     "(zs::ReduceParams)", "norm-only pass over the replicas", launches))
+        if oneshot:
+            out.append(fold)
         out.append((f"void zs::adamw_kernel<{dt}, {pt}, true, {mx}>(zs::AdamParams)",
                     "gated AdamW reducing the replicas again"
                     + (", fused MXFP8" if w.pack else ""), 1))

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ZERO_ABI_VERSION 3
+#define ZERO_ABI_VERSION 4
 #define ZERO_MAX_REPLICAS 64
 
 /* Element types of gradient replicas.  ZERO_MXFP8 replicas (E4M3 codes plus
@@ -69,8 +69,9 @@ enum {
   ZERO_EINVAL = -1, /* null required pointer, P outside [1,64], bad dtype,
                        step < 1, conflicting or missing gradient source */
   ZERO_EALIGN = -2, /* a device pointer is not 16-byte aligned */
-  ZERO_ESIZE = -3,  /* MXFP8 pack with n % 32 != 0, or n >= 2^32 in a call
-                       that adds to a norm accumulator */
+  ZERO_ESIZE = -3,  /* MXFP8 pack with n % 32 != 0, n >= 2^32 in a call
+                       that adds to a norm accumulator, or a workspace below
+                       ZERO_REDUCE_WORKSPACE_BYTES */
   ZERO_EHIP = -4    /* the HIP runtime reported a launch error */
 };
 
@@ -98,6 +99,20 @@ typedef struct zero_norm_acc {
   uint32_t overflow;
 } zero_norm_acc;
 
+/* Optional workspace of zero_shard_reduce and zero_shard_reduce_mx: 512
+ * accumulator slots.  With one, the reduce of 4 or more replicas runs on a
+ * one-shot grid (a few tiles per workgroup, in address order) whose
+ * workgroups add their norm state to the slots, and a one-workgroup kernel
+ * launched after it adds the slots to `acc` and zeroes them again.  Results
+ * are bitwise the same with and without it.  Measured on MI355X it pays for
+ * whole multi-GB shards; for bucket-sized calls (25e6 elements) the extra
+ * launch made it slower, so pass NULL there.  Device memory of at least
+ * ZERO_REDUCE_WORKSPACE_BYTES, 16-byte aligned, zeroed by the caller before
+ * its first use (zero_norm_acc_clear on it as ZERO_REDUCE_WORKSPACE_BYTES /
+ * 64 accumulators does that) and left zeroed by every call.  Calls that
+ * share a workspace must not run concurrently (order them on one stream). */
+#define ZERO_REDUCE_WORKSPACE_BYTES (64 * 512)
+
 /* Zero n_accs accumulators with a fill kernel (safe inside stream capture). */
 int zero_norm_acc_clear(zero_norm_acc *accs, int n_accs, void *stream);
 
@@ -113,10 +128,12 @@ float zero_inv_scale(int P, double loss_scale);
  *             each replica).  dtype ZERO_F32 or ZERO_BF16.
  *   g_out     device fp32[n], or NULL to skip writing the averaged gradient.
  *   acc       device accumulator to add this range's norm state to, or NULL.
+ *   workspace device workspace (ZERO_REDUCE_WORKSPACE_BYTES above) or NULL;
+ *             workspace_bytes its size (ZERO_ESIZE if too small).
  * At least one of g_out and acc must be given. */
 int zero_shard_reduce(const void *const *replicas, int P, int dtype, size_t n,
                       float inv_scale, float *g_out, zero_norm_acc *acc,
-                      void *stream);
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Shard reduce of MXFP8-stored gradient replicas (the "12 percent off stored
  * state" of Zero_From_Scratch's outline item on MXFP8: bf16 gradients kept
@@ -131,10 +148,12 @@ int zero_shard_reduce(const void *const *replicas, int P, int dtype, size_t n,
  *   scales[k]  HOST array of P device pointers to uint8[n/32] scale bytes
  *              (any alignment); for a bucket at element offset `lo` pass
  *              codes + lo and scales + lo/32.
- *   n % 32 == 0 (ZERO_ESIZE otherwise).  g_out / acc as zero_shard_reduce. */
+ *   n % 32 == 0 (ZERO_ESIZE otherwise).  g_out / acc / workspace as
+ *   zero_shard_reduce. */
 int zero_shard_reduce_mx(const uint8_t *const *codes, const uint8_t *const *scales,
                          int P, size_t n, float inv_scale, float *g_out,
-                         zero_norm_acc *acc, void *stream);
+                         zero_norm_acc *acc, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /* Norm state of one buffer: adds the groups of g[i] = grad[i] * inv_scale
  * (grad fp32 or bf16, device) to acc, as zero_shard_reduce with P = 1 and

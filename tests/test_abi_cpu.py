@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     lib.zero_abi_version.restype = C.c_int
-    assert lib.zero_abi_version() == 3
+    assert lib.zero_abi_version() == 4
     lib.zero_strerror.restype = C.c_char_p
     lib.zero_strerror.argtypes = [C.c_int]
     texts = {lib.zero_strerror(s).decode() for s in (0, -1, -2, -3, -4, 7)}
@@ -54,23 +54,38 @@ def test_inv_scale_matches_definition(lib):
 
 def test_argument_checks(lib):
     vp = C.c_void_p
-    lib.zero_shard_reduce.argtypes = [vp, C.c_int, C.c_int, C.c_size_t, C.c_float, vp, vp, vp]
+    lib.zero_shard_reduce.argtypes = [vp, C.c_int, C.c_int, C.c_size_t, C.c_float, vp, vp, vp,
+                                      C.c_size_t, vp]
+    lib.zero_shard_reduce_mx.argtypes = [vp, vp, C.c_int, C.c_size_t, C.c_float, vp, vp, vp,
+                                         C.c_size_t, vp]
     lib.zero_mxfp8_pack.argtypes = [vp, C.c_size_t, vp, vp, vp]
     lib.zero_grad_norm.argtypes = [vp, C.c_int, C.c_size_t, C.c_float, vp, vp]
     lib.zero_adamw_step.argtypes = [vp, vp]
     lib.zero_norm_acc_clear.argtypes = [vp, C.c_int, vp]
     fake = 0x10000                     # aligned, never dereferenced
     reps = (vp * 2)(fake, fake + 0x1000)
-    assert lib.zero_shard_reduce(None, 2, 1, 64, 1.0, fake, None, None) == -1
-    assert lib.zero_shard_reduce(reps, 0, 1, 64, 1.0, fake, None, None) == -1
-    assert lib.zero_shard_reduce(reps, 65, 1, 64, 1.0, fake, None, None) == -1
-    assert lib.zero_shard_reduce(reps, 2, 5, 64, 1.0, fake, None, None) == -1
-    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, None, None, None) == -1
-    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake + 4, None, None) == -2
+    assert lib.zero_shard_reduce(None, 2, 1, 64, 1.0, fake, None, None, 0, None) == -1
+    assert lib.zero_shard_reduce(reps, 0, 1, 64, 1.0, fake, None, None, 0, None) == -1
+    assert lib.zero_shard_reduce(reps, 65, 1, 64, 1.0, fake, None, None, 0, None) == -1
+    assert lib.zero_shard_reduce(reps, 2, 5, 64, 1.0, fake, None, None, 0, None) == -1
+    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, None, None, None, 0, None) == -1
+    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake + 4, None, None, 0, None) == -2
     bad = (vp * 2)(fake, fake + 2)
-    assert lib.zero_shard_reduce(bad, 2, 1, 64, 1.0, fake, None, None) == -2
-    assert lib.zero_shard_reduce(reps, 2, 1, 1 << 32, 1.0, None, fake, None) == -3
-    assert lib.zero_shard_reduce(reps, 2, 1, 0, 1.0, fake, None, None) == 0
+    assert lib.zero_shard_reduce(bad, 2, 1, 64, 1.0, fake, None, None, 0, None) == -2
+    assert lib.zero_shard_reduce(reps, 2, 1, 1 << 32, 1.0, None, fake, None, 0, None) == -3
+    assert lib.zero_shard_reduce(reps, 2, 1, 0, 1.0, fake, None, None, 0, None) == 0
+    # the optional reduce workspace: 16-byte aligned, at least
+    # ZERO_REDUCE_WORKSPACE_BYTES (64 * 512)
+    ws = 64 * 512
+    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake, None, fake + 8, ws, None) == -2
+    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake, None, fake, ws - 1, None) == -3
+    assert lib.zero_shard_reduce(reps, 2, 1, 0, 1.0, fake, fake, fake, ws, None) == 0
+    scales = (vp * 2)(fake + 1, fake + 3)
+    assert lib.zero_shard_reduce_mx(reps, scales, 2, 64, 1.0, fake, None, fake + 8, ws,
+                                    None) == -2
+    assert lib.zero_shard_reduce_mx(reps, scales, 2, 64, 1.0, fake, None, fake, 64,
+                                    None) == -3
+    assert lib.zero_shard_reduce_mx(reps, scales, 2, 0, 1.0, fake, None, fake, ws, None) == 0
     assert lib.zero_grad_norm(None, 1, 64, 1.0, fake, None) == -1
     assert lib.zero_mxfp8_pack(fake, 33, fake, fake, None) == -3
     assert lib.zero_mxfp8_pack(fake, 64, fake, fake + 1, None) == -2

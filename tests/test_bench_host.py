@@ -125,17 +125,22 @@ def test_pass_structure_choice():
 
 
 @pytest.mark.parametrize("name,kernels", [
-    ("30b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, false>(zs::ReduceParams)",
+    ("30b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, false, true>"
+                      "(zs::ReduceParams)",
+                      "zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
                       "void zs::adamw_kernel<-1, 1, true, true>(zs::AdamParams)"]),
-    ("7b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, true>(zs::ReduceParams)",
+    ("7b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, true, false>"
+                     "(zs::ReduceParams)",
                      "void zs::adamw_kernel<-1, 1, true, false>(zs::AdamParams)"]),
-    ("1.3b-unsharded", ["void zs::shard_reduce_kernel<1, 1, false, true, false>(zs::ReduceParams)",
+    ("1.3b-unsharded", ["void zs::shard_reduce_kernel<1, 1, false, true, false, false>"
+                        "(zs::ReduceParams)",
                         "void zs::adamw_kernel<1, 1, true, false>(zs::AdamParams)"]),
     ("flat-1m-p4", ["void zs::adamw_kernel<0, 4, true, false>(zs::AdamParams)"]),
 ])
 def test_step_kernel_names(name, kernels):
     """The kernels a step launches, named as rocprofv3 prints them, follow the
-    pass structure; the 35 buckets of the 7B shard take one reduce each."""
+    pass structure; the 35 buckets of the 7B shard take one reduce each, the
+    whole 30B shard the one-shot reduce and its fold."""
     got = bench.step_kernels(configs.ALL[name])
     assert [k for k, _, _ in got[:-1]] == kernels
     assert got[-1][0].startswith("zs::step_advance_kernel(")

@@ -81,6 +81,22 @@ def test_shard_reduce_and_norm(zs, P, bf16):
         assert same_bits(from_dev(g2), want_g), n
         assert zs.read_norm_acc(acc)[0] == want_acc, (n, zs.read_norm_acc(acc)[0], want_acc)
         assert zs.read_norm_acc(acc2)[0] == want_acc, n
+        # with the workspace (the one-shot grid for P >= 4): the same bits,
+        # and the workspace is zero again after every call
+        ws = zs.new_reduce_workspace()
+        g3 = torch.empty(n, dtype=torch.float32, device="cuda")
+        acc3 = zs.new_norm_acc(1)
+        zs.zero_shard_reduce(dreps, inv, g_out=g3, acc=acc3, workspace=ws)
+        acc4 = zs.new_norm_acc(1)
+        zs.zero_shard_reduce(dreps, inv, acc=acc4, workspace=ws)
+        g4 = torch.empty(n, dtype=torch.float32, device="cuda")
+        zs.zero_shard_reduce(dreps, inv, g_out=g4, workspace=ws)
+        torch.cuda.synchronize()
+        assert same_bits(from_dev(g3), want_g), n
+        assert same_bits(from_dev(g4), want_g), n
+        assert zs.read_norm_acc(acc3)[0] == want_acc, n
+        assert zs.read_norm_acc(acc4)[0] == want_acc, n
+        assert int(ws.abs().sum().item()) == 0, n
 
 
 def test_grad_norm_with_loss_scale(zs):
@@ -106,13 +122,40 @@ def test_buckets_and_grid_shapes_do_not_change_the_norm(zs):
     inv = O.inv_scale(P, 1.0)
     whole = zs.new_norm_acc(1)
     zs.zero_shard_reduce(reps, inv, acc=whole)
+    ws = zs.new_reduce_workspace()
     for bucket in (32, 4096, 32 * 7919, 1 << 20):
-        acc = zs.new_norm_acc(1)
-        for lo in range(0, n, bucket):
-            hi = min(n, lo + bucket)
-            zs.zero_shard_reduce([r[lo:hi] for r in reps], inv, acc=acc)
-        torch.cuda.synchronize()
-        assert zs.read_norm_acc(acc) == zs.read_norm_acc(whole), bucket
+        for workspace in (None, ws):
+            acc = zs.new_norm_acc(1)
+            for lo in range(0, n, bucket):
+                hi = min(n, lo + bucket)
+                zs.zero_shard_reduce([r[lo:hi] for r in reps], inv, acc=acc,
+                                     workspace=workspace)
+            torch.cuda.synchronize()
+            assert zs.read_norm_acc(acc) == zs.read_norm_acc(whole), (bucket, workspace)
+    assert int(ws.abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("P,bf16", [(8, True), (4, False), (16, True)])
+def test_one_shot_reduce_folds_many_slots(zs, P, bf16):
+    """The one-shot form with thousands of workgroups, each slot of the
+    workspace taken by several of them, then a ragged tail; repeated calls
+    reuse the workspace, which each call leaves zero."""
+    import torch
+    n = 2048 * 6007 + 8 * 333 + 3
+    reps = _replicas(P, n, bf16, seed=13, inject=[(0, n - 2, np.nan), (P - 1, 5, -np.inf)])
+    inv = O.inv_scale(P, 1.0)
+    want_g = O.reduce(reps, inv)
+    want_acc = acc_from_oracle(O.norm_accumulate(want_g))
+    dreps = [to_dev(r) for r in reps]
+    ws = zs.new_reduce_workspace()
+    g = torch.empty(n, dtype=torch.float32, device="cuda")
+    accs = zs.new_norm_acc(3)
+    for k in range(3):
+        zs.zero_shard_reduce(dreps, inv, g_out=g, acc=accs[k], workspace=ws)
+    torch.cuda.synchronize()
+    assert same_bits(from_dev(g), want_g), mismatch_report("g", from_dev(g), want_g)
+    assert zs.read_norm_acc(accs) == [want_acc] * 3
+    assert int(ws.abs().sum().item()) == 0
 
 
 @pytest.mark.parametrize("P,bf16", [(4, True), (8, True), (4, False), (8, False)])
@@ -190,11 +233,18 @@ def test_mx_reduce_and_norm(zs, P):
         zs.zero_shard_reduce_mx(codes, scales, inv, g_out=g, acc=acc)
         acc2 = zs.new_norm_acc(1)
         zs.zero_shard_reduce_mx(codes, scales, inv, acc=acc2)
+        ws = zs.new_reduce_workspace()
+        g3 = torch.empty(n, dtype=torch.float32, device="cuda")
+        acc3 = zs.new_norm_acc(1)
+        zs.zero_shard_reduce_mx(codes, scales, inv, g_out=g3, acc=acc3, workspace=ws)
         torch.cuda.synchronize()
         got = from_dev(g)
         assert _same_or_both_nan(got, want_g), mismatch_report(f"g n={n}", got, want_g)
+        assert _same_or_both_nan(from_dev(g3), want_g), n
         assert zs.read_norm_acc(acc)[0] == want_acc, n
         assert zs.read_norm_acc(acc2)[0] == want_acc, n
+        assert zs.read_norm_acc(acc3)[0] == want_acc, n
+        assert int(ws.abs().sum().item()) == 0, n
 
 
 def test_mx_reduce_rejects_bad_sizes(zs):
@@ -722,17 +772,22 @@ def test_device_counter_matches_host_counter(zs):
     assert host.applied_steps() == dev.applied_steps() == 100_000
 
 
-@pytest.mark.parametrize("case", ["buckets", "recompute", "fused"])
-def test_graph_replay_matches_eager(zs, case):
+@pytest.mark.parametrize("case", ["buckets", "recompute", "fused", "oneshot"])
+def test_graph_replay_matches_eager(zs, case, monkeypatch):
     """One step recorded once and replayed: after every replay, with eager
     work and synchronisation between replays, the state is bitwise that of
     the same step run eagerly.  Cases: 8 bf16 replicas in 34 buckets with the
     gate and fused MXFP8 (materialised g, a skipped replay); one bf16 replica
     with a loss scale and the overflow check (recompute path, a skipped
-    replay); 4 fp32 replicas, no gate (one fused pass)."""
+    replay); 4 fp32 replicas, no gate (one fused pass); 8 bf16 replicas on
+    the one-shot reduce, whose workspace each replay leaves zero."""
     import torch
     n = 65536 + 96
-    if case == "buckets":
+    if case == "oneshot":
+        import zero_sharded_mixed_step_amd.step as step_mod
+        monkeypatch.setattr(step_mod, "ONESHOT_MIN", 0)   # the workspace at this size too
+        P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP), 5
+    elif case == "buckets":
         P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, bucket=32 * 61), 4
     elif case == "recompute":
         P, dt, skip_call = 1, torch.bfloat16, 4
@@ -743,7 +798,7 @@ def test_graph_replay_matches_eager(zs, case):
     eager = zs.ShardStep(n, P, dt, device_counter=True, **kw)
     graphed = zs.ShardStep(n, P, dt, device_counter=True, **kw)
     assert eager.path == {"buckets": "materialize", "recompute": "recompute",
-                          "fused": "fused"}[case]
+                          "fused": "fused", "oneshot": "materialize"}[case]
     _init(eager, graphed)
     reps = [torch.empty(n, dtype=torch.int16 if dt == torch.bfloat16 else torch.float32,
                         device="cuda") for _ in range(P)]
@@ -768,6 +823,7 @@ def test_graph_replay_matches_eager(zs, case):
         torch.cuda.synchronize()
         assert _same_state(eager, graphed), call
         assert eager.applied_steps() == graphed.applied_steps()
+        assert int(graphed.reduce_ws.abs().sum().item()) == 0, call
     assert graphed.applied_steps() == (6 if skip_call else 7)
 
 

@@ -13,9 +13,10 @@ import torch
 from . import build as _build
 
 ZERO_F32, ZERO_BF16, ZERO_MXFP8 = 0, 1, 2
-ABI_VERSION = 3        # the zero_step.h this binding's structs follow
+ABI_VERSION = 4        # the zero_step.h this binding's structs follow
 ZERO_MAX_REPLICAS = 64
 ACC_WORDS = 8          # one zero_norm_acc = 64 bytes = 8 int64 words
+REDUCE_WORKSPACE_BYTES = 64 * 512   # ZERO_REDUCE_WORKSPACE_BYTES
 
 _lib = None
 
@@ -53,12 +54,12 @@ def lib():
         L.zero_inv_scale.argtypes = [i, C.c_double]
         L.zero_inv_scale.restype = C.c_float
         L.zero_norm_acc_clear.argtypes = [vp, i, vp]
-        L.zero_shard_reduce.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp]
+        L.zero_shard_reduce.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp, sz, vp]
         L.zero_grad_norm.argtypes = [vp, i, sz, C.c_float, vp, vp]
         L.zero_adamw_step.argtypes = [C.POINTER(_AdamArgs), vp]
         L.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
         L.zero_mxfp8_pack.argtypes = [vp, sz, vp, vp, vp]
-        L.zero_shard_reduce_mx.argtypes = [vp, vp, i, sz, C.c_float, vp, vp, vp]
+        L.zero_shard_reduce_mx.argtypes = [vp, vp, i, sz, C.c_float, vp, vp, vp, sz, vp]
         L.zero_shard_reduce_mx.restype = i
         L.zero_unfused_workspace_bytes.argtypes = [sz, i]
         L.zero_unfused_workspace_bytes.restype = sz
@@ -149,6 +150,23 @@ def zero_inv_scale(P: int, loss_scale: float = 1.0) -> float:
     return lib().zero_inv_scale(int(P), float(loss_scale))
 
 
+def new_reduce_workspace(device="cuda") -> torch.Tensor:
+    """A zeroed reduce workspace (ZERO_REDUCE_WORKSPACE_BYTES, as int64 words
+    so that zero_norm_acc_clear can zero it)."""
+    ws = torch.empty((REDUCE_WORKSPACE_BYTES // 64, ACC_WORDS), dtype=torch.int64, device=device)
+    zero_norm_acc_clear(ws)
+    return ws
+
+
+def _ws_ptr(workspace):
+    if workspace is None:
+        return None, 0
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < REDUCE_WORKSPACE_BYTES:
+        raise ValueError(f"reduce workspace holds {nbytes} bytes, needs {REDUCE_WORKSPACE_BYTES}")
+    return _dev_ptr(workspace, "workspace"), nbytes
+
+
 def new_norm_acc(k: int = 1, device="cuda") -> torch.Tensor:
     """k zeroed accumulators (64 bytes each) as an int64 (k, 8) tensor."""
     acc = torch.empty((k, ACC_WORDS), dtype=torch.int64, device=device)
@@ -177,7 +195,7 @@ def zero_norm_acc_clear(accs: torch.Tensor, stream=None) -> None:
 
 
 def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
-                      stream=None) -> None:
+                      workspace=None, stream=None) -> None:
     reps = list(replicas)
     if not reps:
         raise ValueError("at least one replica")
@@ -190,13 +208,14 @@ def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
     ap, k = _acc_ptr(acc)
     if k > 1:
         raise ValueError("zero_shard_reduce adds to one accumulator")
+    wp, wb = _ws_ptr(workspace)
     _check(lib().zero_shard_reduce(_ptr_array(reps, "replica"), len(reps), _dtype_code(reps[0]),
-                                   n, float(inv_scale), _dev_ptr(g_out, "g_out"), ap,
+                                   n, float(inv_scale), _dev_ptr(g_out, "g_out"), ap, wp, wb,
                                    _stream(stream)), "zero_shard_reduce")
 
 
 def zero_shard_reduce_mx(codes, scales, inv_scale: float, g_out=None, acc=None, n=None,
-                         stream=None) -> None:
+                         workspace=None, stream=None) -> None:
     """Shard reduce of MXFP8-stored replicas: codes[k] uint8[n] and scales[k]
     uint8[n/32] per rank (n % 32 == 0)."""
     codes, scales = list(codes), list(scales)
@@ -210,9 +229,10 @@ def zero_shard_reduce_mx(codes, scales, inv_scale: float, g_out=None, acc=None, 
     ap, k = _acc_ptr(acc)
     if k > 1:
         raise ValueError("zero_shard_reduce_mx adds to one accumulator")
+    wp, wb = _ws_ptr(workspace)
     _check(lib().zero_shard_reduce_mx(_ptr_array(codes, "codes"), _ptr_array(scales, "scales"),
                                       len(codes), n, float(inv_scale), _dev_ptr(g_out, "g_out"),
-                                      ap, _stream(stream)), "zero_shard_reduce_mx")
+                                      ap, wp, wb, _stream(stream)), "zero_shard_reduce_mx")
 
 
 def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:

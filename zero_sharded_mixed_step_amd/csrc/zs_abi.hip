@@ -29,6 +29,13 @@ int check_replicas(const void* const* replicas, int P, int dtype) {
   return ZERO_OK;
 }
 
+int check_workspace(const void* workspace, size_t workspace_bytes) {
+  if (workspace == nullptr) return ZERO_OK;
+  if (!aligned16(workspace)) return ZERO_EALIGN;
+  if (workspace_bytes < ZERO_REDUCE_WORKSPACE_BYTES) return ZERO_ESIZE;
+  return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -42,7 +49,7 @@ const char* zero_strerror(int status) {
                              "gradient source)";
     case ZERO_EALIGN: return "device pointer not 16-byte aligned";
     case ZERO_ESIZE: return "size not supported (MXFP8 needs n % 32 == 0; a norm call needs "
-                            "n < 2^32)";
+                            "n < 2^32; a reduce workspace needs ZERO_REDUCE_WORKSPACE_BYTES)";
     case ZERO_EHIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -66,16 +73,19 @@ int zero_norm_acc_clear(zero_norm_acc* accs, int n_accs, void* stream) {
 }
 
 int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, float inv_scale,
-                      float* g_out, zero_norm_acc* acc, void* stream) {
+                      float* g_out, zero_norm_acc* acc, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   try {
     const int rc = check_replicas(replicas, P, dtype);
     if (rc != ZERO_OK) return rc;
     if (g_out == nullptr && acc == nullptr) return ZERO_EINVAL;
     if ((g_out && !aligned16(g_out)) || (acc && !aligned16(acc))) return ZERO_EALIGN;
+    const int wc = check_workspace(workspace, workspace_bytes);
+    if (wc != ZERO_OK) return wc;
     if (acc != nullptr && n >= (size_t(1) << 32)) return ZERO_ESIZE;
     if (n == 0) return ZERO_OK;
-    return status_of(
-        zs::launch_reduce(replicas, P, dtype, n, inv_scale, g_out, acc, as_stream(stream)));
+    return status_of(zs::launch_reduce(replicas, P, dtype, n, inv_scale, g_out, acc,
+                                       as_stream(stream), nullptr, workspace));
   } catch (...) {
     return ZERO_EHIP;
   }
@@ -83,7 +93,7 @@ int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, f
 
 int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scales, int P,
                          size_t n, float inv_scale, float* g_out, zero_norm_acc* acc,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (codes == nullptr || scales == nullptr || P < 1 || P > ZERO_MAX_REPLICAS)
       return ZERO_EINVAL;
@@ -93,6 +103,8 @@ int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scal
     }
     if (g_out == nullptr && acc == nullptr) return ZERO_EINVAL;
     if ((g_out && !aligned16(g_out)) || (acc && !aligned16(acc))) return ZERO_EALIGN;
+    const int wc = check_workspace(workspace, workspace_bytes);
+    if (wc != ZERO_OK) return wc;
     if (n % 32 != 0 || (acc != nullptr && n >= (size_t(1) << 32))) return ZERO_ESIZE;
     if (n == 0) return ZERO_OK;
     const void* c[ZERO_MAX_REPLICAS];
@@ -102,7 +114,7 @@ int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scal
       sc[k] = scales[k];
     }
     return status_of(zs::launch_reduce(c, P, ZERO_MXFP8, n, inv_scale, g_out, acc,
-                                       as_stream(stream), sc));
+                                       as_stream(stream), sc, workspace));
   } catch (...) {
     return ZERO_EHIP;
   }

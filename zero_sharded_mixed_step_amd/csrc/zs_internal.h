@@ -71,7 +71,8 @@ int compute_units(int device);
 // dtype ZERO_MXFP8: replicas are the code arrays and mx_scales the scales.
 hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t n,
                          float inv_scale, float* g_out, zero_norm_acc* acc,
-                         hipStream_t stream, const void* const* mx_scales = nullptr);
+                         hipStream_t stream, const void* const* mx_scales = nullptr,
+                         void* workspace = nullptr);
 
 struct AdamLaunch {
   const float* grad;

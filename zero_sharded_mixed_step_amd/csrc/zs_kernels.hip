@@ -68,7 +68,66 @@ struct ReduceParams {
   uint64_t nchunks;
   float* g_out;
   zero_norm_acc* acc;
+  // One-shot form with a norm: the caller's workspace, kReduceSlots
+  // accumulators.
+  zero_norm_acc* slots;
 };
+
+// Accumulators of the one-shot reduce: workgroup b adds its norm state to
+// slot b % kReduceSlots, which spreads the integer atomics over as many
+// cache lines; on one line they serialise (about 12 ns each measured on
+// MI355X, far slower than the stream).  A one-workgroup kernel launched
+// next on the stream folds the slots into the caller's accumulator and
+// clears them; the launch boundary orders the two, so neither needs a
+// fence (an agent-scope fence per workgroup, which writes back L2, made the
+// pass four times slower).
+constexpr int kReduceSlots = ZERO_REDUCE_WORKSPACE_BYTES / 64;
+static_assert(kReduceSlots >= kThreads && sizeof(zero_norm_acc) == 64, "workspace layout");
+
+// Sum over the 64 lanes of a wave (every lane receives it).
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Per-workgroup totals of a norm state (7 digits, non-finite and overflow
+// counts, each in the matching lane-private LDS row or register) reduced
+// across the workgroup: every lane of wave 0 gets them in tot[].
+__device__ __forceinline__ void workgroup_norm_totals(const uint64_t (*s_digit)[kThreads],
+                                                      uint64_t extra0, uint64_t extra1,
+                                                      uint64_t (*s_part)[9], uint64_t tot[9]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint64_t v[9];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) v[k] = s_digit[k][tid];  // this lane's own row
+  v[7] = extra0;
+  v[8] = extra1;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) v[k] = wave_sum_u64(v[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) s_part[wave][k] = v[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    uint64_t t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t += s_part[w][k];
+    tot[k] = t;
+  }
+}
+
+// Adds totals (7 digits, counts) to an accumulator; zero parts are skipped.
+__device__ __forceinline__ void acc_add(zero_norm_acc* acc, const uint64_t tot[9]) {
+#pragma unroll
+  for (int k = 0; k < 7; ++k)
+    if (tot[k] != 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&acc->digit[k]),
+                static_cast<unsigned long long>(tot[k]));
+  if (tot[7] != 0) atomicAdd(&acc->nonfinite, static_cast<uint32_t>(tot[7]));
+  if (tot[8] != 0) atomicAdd(&acc->overflow, static_cast<uint32_t>(tot[8]));
+}
 
 #ifndef ZS_REDUCE_LOADS
 #define ZS_REDUCE_LOADS 24
@@ -81,11 +140,27 @@ struct ReduceParams {
 #endif
 
 
-template <int DT, int PT, bool WRITE, bool NORM, bool PIPE>
+#ifndef ZS_REDUCE_ONESHOT_LOADS
+#define ZS_REDUCE_ONESHOT_LOADS 16
+#endif
+
+// Tiles per workgroup iteration of the reduce: about `loads` 16-byte loads
+// per lane (P of them per bf16 tile, 2P per fp32 tile; 8 assumed for a
+// replica count only known at run time), between 1 and 8.
+template <int DT, int PT>
+constexpr int reduce_tiles_per_step(int loads) {
+  const int raw = PT > 0 ? PT * (DT == ZERO_F32 ? 2 : 1) : 8;
+  return loads / raw < 1 ? 1 : (loads / raw > 8 ? 8 : loads / raw);
+}
+
+// ONESHOT: a one-shot grid of about ZS_REDUCE_ONESHOT_LOADS 16-byte loads
+// per lane per workgroup; with NORM, per-workgroup state goes to prm.slots.
+template <int DT, int PT, bool WRITE, bool NORM, bool PIPE, bool ONESHOT>
 __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm) {
   static_assert(!PIPE || PT >= 4, "the pipelined fast path is built for 4 or 8 replicas");
+  static_assert(!(PIPE && ONESHOT), "one loop form per kernel");
   __shared__ uint64_t s_digit[NORM ? 7 : 1][kThreads];
-  __shared__ uint32_t s_count[NORM ? 2 : 1][kThreads];
+  __shared__ uint32_t s_count[(NORM && !ONESHOT) ? 2 : 1][kThreads];
   const int tid = threadIdx.x;
   const int quad_lane = tid & 3;
   if constexpr (NORM) {
@@ -145,10 +220,8 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
   // loads per stage, on one workgroup per compute unit.  Otherwise about
   // ZS_REDUCE_LOADS loads are issued, then consumed.
   constexpr bool kPipe = PIPE;
-  constexpr int kRawLoads = PT > 0 ? PT * (DT == ZERO_F32 ? 2 : 1) : 8;
-  constexpr int kLoads = kPipe ? ZS_REDUCE_PIPE_LOADS : ZS_REDUCE_LOADS;
-  constexpr int U = kLoads / kRawLoads < 1 ? 1
-                    : (kLoads / kRawLoads > 8 ? 8 : kLoads / kRawLoads);
+  constexpr int U = reduce_tiles_per_step<DT, PT>(
+      kPipe ? ZS_REDUCE_PIPE_LOADS : (ONESHOT ? ZS_REDUCE_ONESHOT_LOADS : ZS_REDUCE_LOADS));
   const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
   const uint64_t full_tiles = prm.n / (static_cast<uint64_t>(kThreads) * kVec);
   const uint64_t step = static_cast<uint64_t>(gridDim.x) * U;
@@ -228,7 +301,13 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
       if constexpr (NORM) norm_chunk(g);
     }
   }
-  if constexpr (NORM) {
+  if constexpr (NORM && ONESHOT) {
+    // Workgroup totals into slot blockIdx % kReduceSlots.
+    __shared__ uint64_t s_part[kThreads / 64][9];
+    uint64_t tot[9];
+    workgroup_norm_totals(s_digit, nonfinite, overflow, s_part, tot);
+    if (tid == 0) acc_add(prm.slots + blockIdx.x % kReduceSlots, tot);
+  } else if constexpr (NORM) {
   s_count[0][tid] = nonfinite;
   s_count[1][tid] = overflow;
   __syncthreads();
@@ -255,36 +334,74 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
   }
 }
 
-template <int DT, int PT, bool PIPE>
+// Adds the slots of a one-shot reduce to acc and zeroes them (one
+// workgroup; each slot field is read and cleared by one atomic exchange).
+__global__ void __launch_bounds__(kThreads) slot_fold_kernel(zero_norm_acc* slots,
+                                                             zero_norm_acc* acc) {
+  __shared__ uint64_t s_rows[7][kThreads];
+  __shared__ uint64_t s_part[kThreads / 64][9];
+  const int tid = threadIdx.x;
+  uint64_t mine[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  for (int sl = tid; sl < kReduceSlots; sl += kThreads) {
+    zero_norm_acc* a = slots + sl;
+#pragma unroll
+    for (int k = 0; k < 7; ++k)
+      mine[k] += atomicExch(reinterpret_cast<unsigned long long*>(&a->digit[k]), 0ull);
+    mine[7] += atomicExch(&a->nonfinite, 0u);
+    mine[8] += atomicExch(&a->overflow, 0u);
+  }
+#pragma unroll
+  for (int k = 0; k < 7; ++k) s_rows[k][tid] = mine[k];
+  uint64_t tot[9];
+  workgroup_norm_totals(s_rows, mine[7], mine[8], s_part, tot);
+  if (tid == 0) acc_add(acc, tot);
+}
+
+template <int DT, int PT, bool PIPE, bool ONESHOT>
 static void reduce_launch(const ReduceParams& prm, bool write, bool norm, unsigned grid,
                           hipStream_t st) {
   if (write && norm)
-    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, true, PIPE>), dim3(grid),
+    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, true, PIPE, ONESHOT>), dim3(grid),
                        dim3(kThreads), 0, st, prm);
   else if (write)
-    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, false, PIPE>), dim3(grid),
+    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, true, false, PIPE, ONESHOT>), dim3(grid),
                        dim3(kThreads), 0, st, prm);
   else
-    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, false, true, PIPE>), dim3(grid),
+    hipLaunchKernelGGL((shard_reduce_kernel<DT, PT, false, true, PIPE, ONESHOT>), dim3(grid),
                        dim3(kThreads), 0, st, prm);
 }
 
-// Below ZS_REDUCE_PIPE_MAX_ELEMS elements (a bucket) the pipelined form on
-// one workgroup per CU measured faster with 4 or 8 replicas; above it (a whole
-// multi-GB shard) the unpipelined form on ZS_REDUCE_BLOCKS_PER_CU did.  Both
-// compute the same bits.
+// Loop forms, all computing the same bits.  With 4 or more replicas and a
+// workspace, the one-shot grid: on MI355X the 30B-shard reduce (8 bf16
+// replicas, 3.75e9 elements) ran at 5.9 TB/s on it against 5.6 on the
+// persistent grid; for 25e6-element buckets, the extra fold launch per
+// bucket made it slower than the pipelined form (so callers pass no
+// workspace there).  Without a workspace, below ZS_REDUCE_PIPE_MAX_ELEMS
+// elements (a bucket) the pipelined form on one workgroup per CU measured
+// faster with 4 or 8 replicas; above it the unpipelined form on
+// ZS_REDUCE_BLOCKS_PER_CU did.  With one to three replicas the pass is bound
+// by the norm's arithmetic, and the persistent grid, which meets the atomics
+// once per workgroup, stays.
 template <int DT, int PT>
 static void reduce_dispatch_io(const ReduceParams& prm, bool write, bool norm,
                                hipStream_t st) {
+  if ((PT >= 4 || (PT == 0 && prm.P >= 4)) && prm.slots != nullptr) {
+    constexpr int U = reduce_tiles_per_step<DT, PT>(ZS_REDUCE_ONESHOT_LOADS);
+    reduce_launch<DT, PT, false, true>(prm, write, norm, grid_oneshot(prm.nchunks, U), st);
+    if (norm)
+      hipLaunchKernelGGL(slot_fold_kernel, dim3(1), dim3(kThreads), 0, st, prm.slots, prm.acc);
+    return;
+  }
   if constexpr (PT >= 4) {
     if (prm.n <= static_cast<uint64_t>(ZS_REDUCE_PIPE_MAX_ELEMS)) {
-      reduce_launch<DT, PT, true>(prm, write, norm,
-                                  grid_for(prm.nchunks, ZS_REDUCE_PIPE_BLOCKS_PER_CU), st);
+      reduce_launch<DT, PT, true, false>(prm, write, norm,
+                                         grid_for(prm.nchunks, ZS_REDUCE_PIPE_BLOCKS_PER_CU),
+                                         st);
       return;
     }
   }
-  reduce_launch<DT, PT, false>(prm, write, norm,
-                               grid_for(prm.nchunks, ZS_REDUCE_BLOCKS_PER_CU), st);
+  reduce_launch<DT, PT, false, false>(prm, write, norm,
+                                      grid_for(prm.nchunks, ZS_REDUCE_BLOCKS_PER_CU), st);
 }
 
 template <int DT>
@@ -300,8 +417,9 @@ static void reduce_dispatch_p(const ReduceParams& prm, bool write, bool norm, hi
 
 hipError_t launch_reduce(const void* const* replicas, int P, int dtype, uint64_t n,
                          float inv_scale, float* g_out, zero_norm_acc* acc,
-                         hipStream_t stream, const void* const* mx_scales) {
+                         hipStream_t stream, const void* const* mx_scales, void* workspace) {
   ReduceParams prm;
+  prm.slots = static_cast<zero_norm_acc*>(workspace);
   prm.R = pack_replicas(replicas, P);
   if (mx_scales != nullptr)
     for (int k = 0; k < P; ++k) prm.R.s[k] = mx_scales[k];

@@ -60,6 +60,12 @@ def choose_path(P: int, g_b: float, gated: bool, mx_grads: bool = False,
     return path
 
 
+# Reduce launches above this many elements take the one-shot form (the
+# library's workspace); bucket-sized ones (the 7B shard's 25e6) ran faster
+# on the persistent pipelined form, without the extra fold launch.
+ONESHOT_MIN = 1 << 27
+
+
 class ShardStep:
     def __init__(self, n: int, P: int, grad_dtype: torch.dtype, *, lr: float,
                  beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
@@ -91,6 +97,10 @@ class ShardStep:
         self.g = (torch.empty(self.n, dtype=torch.float32, device=dev)
                   if path == "materialize" else None)
         self.acc = B.new_norm_acc(1, dev)
+        # The reduce's one-shot workspace, for launches above ONESHOT_MIN
+        # elements: zeroed here, left zeroed by every reduce call (so a
+        # recorded graph replays without clearing it).
+        self.reduce_ws = B.new_reduce_workspace(dev)
         self.skipped = torch.zeros(1, dtype=torch.int32, device=dev)
         self._skip_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
         self._skip_event = None
@@ -132,17 +142,19 @@ class ShardStep:
         if self.path == "fused":
             return
         for lo, hi in self._ranges():
+            ws = self.reduce_ws if hi - lo > ONESHOT_MIN else None
             if self.mx_grads:
                 codes = [c[lo:hi] for c, _ in replicas]
                 scales = [sc[lo // 32:hi // 32] for _, sc in replicas]
                 B.zero_shard_reduce_mx(codes, scales, self.inv_scale, g_out=self.g[lo:hi],
-                                       acc=self.acc)
+                                       acc=self.acc, workspace=ws)
                 continue
             views = [r[lo:hi] for r in replicas]
             if self.path == "materialize":
-                B.zero_shard_reduce(views, self.inv_scale, g_out=self.g[lo:hi], acc=self.acc)
+                B.zero_shard_reduce(views, self.inv_scale, g_out=self.g[lo:hi], acc=self.acc,
+                                    workspace=ws)
             else:
-                B.zero_shard_reduce(views, self.inv_scale, acc=self.acc)
+                B.zero_shard_reduce(views, self.inv_scale, acc=self.acc, workspace=ws)
 
     def _resolve_pending_skip(self) -> None:
         if self._skip_event is not None:
