@@ -56,9 +56,9 @@ __host__ __device__ inline AdamScalars derive_adam_scalars(const AdamHyper& h, i
 // persistent grid, from sweeps of 1..10 on MI355X: it needs 4 to keep enough
 // loads in flight, except for bucket-sized launches with 4 or 8 replicas,
 // whose software-pipelined fast path holds twice the loads per lane and runs
-// best at 1.  (The reduce stays persistent: each workgroup ends with atomic
-// adds to the one norm accumulator, which a one-shot grid would multiply.
-// AdamW and the pack launch one-shot grids.)
+// best at 1.  (Without a workspace the reduce stays persistent: each
+// workgroup ends with atomic adds to the one norm accumulator, which a
+// one-shot grid would multiply.  AdamW and the pack launch one-shot grids.)
 #ifndef ZS_REDUCE_BLOCKS_PER_CU
 #define ZS_REDUCE_BLOCKS_PER_CU 4
 #endif

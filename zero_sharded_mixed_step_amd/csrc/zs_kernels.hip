@@ -1,11 +1,13 @@
 // zs_kernels.hip -- the optimizer step's HIP kernels for CDNA4 (gfx950).
 //
 // All four are HBM-bandwidth-bound streaming passes (no matrix work, so no
-// MFMA): 16-byte vector loads/stores per lane over 2048-element tiles.  The
-// reduce runs a persistent grid of a few workgroups per compute unit, so its
-// norm state (reduced in registers by quad DPP, then in lane-private LDS
-// rows) meets one set of integer atomics per workgroup; AdamW and the pack
-// run one-shot grids of a few tiles per workgroup.
+// MFMA): 16-byte vector loads/stores per lane over 2048-element tiles.
+// AdamW, the pack and (given a workspace) the reduce of 4 or more replicas
+// run one-shot grids of a few tiles per workgroup; the reduce's norm state
+// (reduced in registers by quad DPP, then in lane-private LDS rows) then
+// goes to workspace slots that a one-workgroup kernel folds.  Other reduce
+// launches run a persistent grid of a few workgroups per compute unit, each
+// ending with one set of integer atomics on the accumulator.
 #include "zs_device.h"
 #include "zs_internal.h"
 
@@ -40,8 +42,8 @@ static unsigned grid_for(uint64_t nchunks, int blocks_per_cu) {
 // hardware dispatcher hands out tiles in address order and the stream's
 // front stays compact.  Measured on MI355X, write-heavy streams run faster
 // this way than on a persistent grid that strides over the array: a plain
-// 15 GB write 6.8 vs 5.5-5.8 TB/s, the AdamW pass 2-6 % and the MXFP8 pack
-// 10 % faster, with bitwise the same results.  Grids beyond the dispatch
+// 15 GB write 6.8 vs 5.5-5.8 TB/s, the AdamW pass 2-6 %, the MXFP8 pack
+// 10 % and the whole-shard reduce 5 % faster, with bitwise the same results.  Grids beyond the dispatch
 // limit (2^32 work-items) are capped; the kernels' grid-stride loops then
 // take the rest.
 static unsigned grid_oneshot(uint64_t nchunks, int u) {
@@ -91,9 +93,10 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// Per-workgroup totals of a norm state (7 digits, non-finite and overflow
-// counts, each in the matching lane-private LDS row or register) reduced
-// across the workgroup: every lane of wave 0 gets them in tot[].
+// Per-workgroup totals of a norm state (7 digits from the lanes' own LDS
+// rows, the non-finite and overflow counts from registers), reduced across
+// the workgroup by wave shuffles and one LDS exchange: every lane gets them
+// in tot[].  Ends with the workgroup past a barrier.
 __device__ __forceinline__ void workgroup_norm_totals(const uint64_t (*s_digit)[kThreads],
                                                       uint64_t extra0, uint64_t extra1,
                                                       uint64_t (*s_part)[9], uint64_t tot[9]) {
