@@ -109,8 +109,10 @@ typedef struct zero_norm_acc {
  * launch made it slower, so pass NULL there.  Device memory of at least
  * ZERO_REDUCE_WORKSPACE_BYTES, 16-byte aligned, zeroed by the caller before
  * its first use (zero_norm_acc_clear on it as ZERO_REDUCE_WORKSPACE_BYTES /
- * 64 accumulators does that) and left zeroed by every call.  Calls that
- * share a workspace must not run concurrently (order them on one stream). */
+ * 64 accumulators does that) and left zeroed by every call that returns
+ * ZERO_OK; after any other status, zero it again before reusing it.  Calls
+ * that share a workspace must not run concurrently (order them on one
+ * stream). */
 #define ZERO_REDUCE_WORKSPACE_BYTES (64 * 512)
 
 /* Zero n_accs accumulators with a fill kernel (safe inside stream capture). */

@@ -35,6 +35,18 @@ def test_exports_every_declared_symbol(lib):
     assert not missing, missing
 
 
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's constants."""
+    from zero_sharded_mixed_step_amd import _binding as B
+    text = open(HEADER).read()
+    consts = {m.group(1): m.group(2) for m in
+              re.finditer(r"#define (ZERO_[A-Z_]+) (.+)", text)}
+    assert int(consts["ZERO_ABI_VERSION"]) == B.ABI_VERSION
+    assert int(consts["ZERO_MAX_REPLICAS"]) == B.ZERO_MAX_REPLICAS
+    a, b = re.fullmatch(r"\((\d+) \* (\d+)\)", consts["ZERO_REDUCE_WORKSPACE_BYTES"]).groups()
+    assert int(a) * int(b) == B.REDUCE_WORKSPACE_BYTES
+
+
 def test_version_and_status_strings(lib):
     lib.zero_abi_version.restype = C.c_int
     assert lib.zero_abi_version() == 4
