@@ -43,7 +43,7 @@ static unsigned grid_for(uint64_t nchunks, int blocks_per_cu) {
 // front stays compact.  Measured on MI355X, write-heavy streams run faster
 // this way than on a persistent grid that strides over the array: a plain
 // 15 GB write 6.8 vs 5.5-5.8 TB/s, the AdamW pass 2-6 %, the MXFP8 pack
-// 10 % and the whole-shard reduce 5 % faster, with bitwise the same results.  Grids beyond the dispatch
+// 15 % and the whole-shard reduce 5 % faster, with bitwise the same results.  Grids beyond the dispatch
 // limit (2^32 work-items) are capped; the kernels' grid-stride loops then
 // take the rest.
 static unsigned grid_oneshot(uint64_t nchunks, int u) {
@@ -707,11 +707,12 @@ hipError_t launch_acc_clear(zero_norm_acc* accs, int n_accs, hipStream_t stream)
 // -------------------------------------------------------------- MXFP8 ----
 
 #ifndef ZS_MX_UNROLL
-#define ZS_MX_UNROLL 8
+#define ZS_MX_UNROLL 1
 #endif
 
-// ZS_MX_UNROLL tiles per iteration, so that several 16-byte loads per lane
-// are in flight before the integer encoding starts.
+// ZS_MX_UNROLL tiles per workgroup iteration.  On the one-shot grid one tile
+// per workgroup measured fastest on MI355X (30B shard: 1.87 ms against 1.91
+// for 2 tiles and 2.00 for 8; on the persistent grid 8 had been best).
 __global__ void __launch_bounds__(kThreads) mxfp8_kernel(const uint16_t* in, uint64_t nchunks,
                                                          uint8_t* elem, uint8_t* scale,
                                                          const Gate* gate) {
