@@ -70,10 +70,12 @@ __global__ void __launch_bounds__(kThreads) unfused_kernel(UnfusedParams prm) {
   }
 }
 
+// One tile per workgroup (a one-shot grid, as the fused passes use), capped
+// at the dispatch limit; the kernel's grid-stride loop takes any rest.
 template <int OP>
 hipError_t run(const UnfusedParams& prm, hipStream_t st) {
   uint64_t blocks = (prm.nchunks + kThreads - 1) / kThreads;
-  const uint64_t cap = 256ull * 8;
+  const uint64_t cap = 0xFFFFFFFFull / kThreads;
   if (blocks > cap) blocks = cap;
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(unfused_kernel<OP>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
@@ -85,9 +87,12 @@ uint64_t round256(uint64_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
+// Layout: the gate (256 B), 1 + n_other_accs accumulators, the reduce
+// workspace (its slots are never touched: the chain's sum pass keeps no norm,
+// but the workspace selects the one-shot reduce), then two fp32[n] buffers.
 uint64_t unfused_workspace_bytes(uint64_t n, int n_other_accs) {
   return 256 + round256(static_cast<uint64_t>(1 + n_other_accs) * sizeof(zero_norm_acc)) +
-         2 * round256(n * sizeof(float));
+         round256(ZERO_REDUCE_WORKSPACE_BYTES) + 2 * round256(n * sizeof(float));
 }
 
 hipError_t launch_unfused(const AdamLaunch& a, const zero_norm_acc* other_accs,
@@ -95,8 +100,9 @@ hipError_t launch_unfused(const AdamLaunch& a, const zero_norm_acc* other_accs,
   char* ws = static_cast<char*>(workspace);
   Gate* gate = reinterpret_cast<Gate*>(ws);
   zero_norm_acc* accs = reinterpret_cast<zero_norm_acc*>(ws + 256);
-  float* ws0 = reinterpret_cast<float*>(
-      ws + 256 + round256(static_cast<uint64_t>(1 + n_other_accs) * sizeof(zero_norm_acc)));
+  char* reduce_ws =
+      ws + 256 + round256(static_cast<uint64_t>(1 + n_other_accs) * sizeof(zero_norm_acc));
+  float* ws0 = reinterpret_cast<float*>(reduce_ws + round256(ZERO_REDUCE_WORKSPACE_BYTES));
   float* ws1 = ws0 + round256(a.n * sizeof(float)) / sizeof(float);
   hipError_t e;
   UnfusedParams prm{};
@@ -107,7 +113,8 @@ hipError_t launch_unfused(const AdamLaunch& a, const zero_norm_acc* other_accs,
   const float* g = a.grad;
   if (a.replicas != nullptr) {
     // pass 1: s = r_0 + ... + r_{P-1};  pass 2: g = s * inv_scale
-    if ((e = launch_reduce(a.replicas, a.P, a.dtype, a.n, 1.0f, ws0, nullptr, st)) != hipSuccess)
+    if ((e = launch_reduce(a.replicas, a.P, a.dtype, a.n, 1.0f, ws0, nullptr, st, nullptr,
+                           reduce_ws)) != hipSuccess)
       return e;
     prm.a = ws0;
     prm.out = ws1;
