@@ -157,3 +157,55 @@ def test_traffic_report_ratios(capsys):
     assert len(rows) == 5
     for r in rows:
         assert 0.99 < float(r[-1]) < 1.03, r
+
+
+def test_trace_report_reads_a_kernel_stats_file(tmp_path, capsys):
+    """The kernel-trace summary: rocprofv3's stats rows, the step kernels with
+    their averages, and the bench line (with its command) of the same run."""
+    w = configs.SHARD_30B
+    names = [k for k, _, _ in bench.step_kernels(w)]
+    d = tmp_path / "prof"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                     "MaxNs", "StdDev"])
+        for i, n in enumerate(names):
+            wr.writerow([n, 12, 12 * (i + 1) * 1000, (i + 1) * 1000.0, 10.0, 1, 2, 0.5])
+    log = tmp_path / "run.log"
+    log.write_text("noise\n" + json.dumps({"metric": "m", "command": "python bench.py --steps 3"})
+                   + "\n")
+    bench.trace_report(w, str(d), str(log))
+    out = capsys.readouterr().out
+    assert "-- python3 $R/bench.py --steps 3" in out
+    assert "NOT IN THE TABLE" not in out
+    for i, n in enumerate(names):
+        assert f"{n.split('(')[0]}:" in out and f"{(i + 1) * 1000} ns" in out
+    assert out.rstrip().endswith('"command": "python bench.py --steps 3"}')
+
+
+def test_placement_report_splits_the_two_placements(tmp_path, capsys):
+    """Per-launch counters: the first half of the reduce/AdamW launches is the
+    first placement, the second half the one after the spacer; other kernels
+    (the fold, fills) are left out."""
+    d = tmp_path / "pmc"
+    d.mkdir()
+    rows = []
+    kinds = ["void zs::shard_reduce_kernel<1, 8, true, true, false, true>(zs::ReduceParams)",
+             "zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
+             "void zs::adamw_kernel<-1, 1, true, true>(zs::AdamParams)"] * 2
+    for i, k in enumerate(kinds):
+        rows.append({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": "X_sum",
+                     "Counter_Value": 100 + i, "Start_Timestamp": 0,
+                     "End_Timestamp": (i + 1) * 1_000_000})
+    with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        wr.writeheader()
+        wr.writerows(rows)
+    log = tmp_path / "p.log"
+    log.write_text('{"placement": "first"}\n{"placement": "after spacer"}\n')
+    bench.placement_report([str(d), str(log)])
+    lines = [ln.split() for ln in capsys.readouterr().out.splitlines() if ln.startswith("  ")]
+    assert [(r[0], r[1], r[-1]) for r in lines] == [
+        ("first", "reduce", "100"), ("first", "adamw", "102"),
+        ("spacer", "reduce", "103"), ("spacer", "adamw", "105")]
