@@ -120,15 +120,6 @@ class ShardStep:
     def gated(self) -> bool:
         return self.max_norm > 0 or self.check_overflow
 
-    def bytes_per_element(self, g_b: int) -> int:
-        """Fused-minimum HBM bytes per shard element of this step's passes."""
-        fixed = 26
-        if self.path == "fused":
-            return self.P * g_b + fixed
-        if self.path == "materialize":
-            return self.P * g_b + 8 + fixed
-        return 2 * self.P * g_b + fixed
-
     def _ranges(self):
         if self.bucket is None:
             yield 0, self.n
