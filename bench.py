@@ -255,11 +255,13 @@ def trace_report(w, prof_dir, bench_log):
     if line and "command" in json.loads(line):
         args = json.loads(line)["command"].split()[2:]
         cmd = cmd.split(" -- ")[0] + " -- python3 $R/bench.py" + "".join(" " + a for a in args)
+    tag = os.path.basename(os.path.normpath(prof_dir))
+    cmd = cmd.replace("prof_<TAG>", tag) + f" > $R/gpurun_out/{os.path.basename(bench_log)} 2>&1"
     print(f"# rocprofv3 kernel-trace summary: optimizer step, {w.name} ({w.title})")
     print("# MI355X (gfx950), one GPU.  Data (run from /tmp with TMPDIR=/tmp, repo at $R):")
     print("#   " + cmd)
-    print(f"# This summary: python bench.py --trace-report <prof dir> <log of that run> "
-          f"--config {w.name}")
+    print(f"# This summary: python bench.py --trace-report gpurun_out/{tag} "
+          f"gpurun_out/{os.path.basename(bench_log)} --config {w.name}")
     print(f"# Pass structure: {_path_of(w)}; bucket: {w.bucket}.  Durations in ns.  The run "
           "also times the unfused chain (unfused_kernel<..>, gate_kernel, and")
     print("# shard_reduce_kernel / mxfp8_kernel launches of the chain); fill_kernel is the "
@@ -294,11 +296,16 @@ def traffic_report(names):
           "for CTR in FETCH_SIZE WRITE_SIZE:")
     print("#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/pmc_copy_$CTR -o run "
           "-- python3 $R/bench.py --copy-calibration")
-    print("#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/pmc_<TAG>_$CTR -o run "
-          "-- python3 $R/bench.py --config <WORKLOAD> --steps 2 --warmup 1 --no-cpu-baseline "
-          "--no-unfused")
-    print("# Scaled (no GPU): python bench.py --summarize-pmc pmc_<TAG>_FETCH_SIZE "
-          "pmc_<TAG>_WRITE_SIZE pmc_copy_FETCH_SIZE pmc_copy_WRITE_SIZE --config <WORKLOAD>")
+    import re
+    for n in names:
+        m = re.search(r"gpurun_out/(pmc_\w+?)_FETCH_SIZE", data[n]["command"])
+        tag = m.group(1) if m else "pmc_<TAG>"
+        print(f"#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/{tag}_$CTR -o run "
+              f"-- python3 $R/bench.py --config {n} --steps 2 --warmup 1 --no-cpu-baseline "
+              "--no-unfused")
+    print("# Scaled (no GPU), the commands recorded in profiles/hbm_traffic.json:")
+    for n in names:
+        print("#   python " + data[n]["command"])
     print("#   -> profiles/hbm_traffic.json; this table: python bench.py --traffic-report "
           + " ".join(names))
     print("# HBM bytes = 1024 * (FETCH_SIZE * f + WRITE_SIZE * w); a plain 1 GiB copy reads "
@@ -340,11 +347,9 @@ def placement_report(pairs):
     print("# allocated first in the process, then again after a held, written spacer "
           "(bench.py --placement-probe GB).")
     print("# MI355X (gfx950), one GPU.  One counter pass per run (its own process, from /tmp "
-          "with TMPDIR=/tmp, repo at $R):")
-    print("#   rocprofv3 --pmc <COUNTERS> --output-format csv -d $R/gpurun_out/<DIR> -o run "
-          "-- python3 $R/bench.py --placement-probe 60")
-    print("# This summary: python bench.py --placement-report " + " ".join(
-        f"<DIR{i}> <LOG{i}>" for i in range(1, len(runs) + 1)))
+          "with TMPDIR=/tmp, repo at $R); each pass below gives its command.")
+    print("# This summary (from gpurun_out): python bench.py --placement-report " + " ".join(
+        f"{os.path.basename(os.path.normpath(d))} {os.path.basename(lg)}" for d, lg in runs))
     print("# Launch durations (ms) are rocprofv3's per-dispatch timestamps under counter "
           "collection.  TCC_EA0 DRAM read requests are 128 B, write requests 64 B; GMI = "
           "inter-die.")
@@ -365,8 +370,15 @@ def placement_report(pairs):
                 names.append(c)
             e[c] = float(r["Counter_Value"])
         order = [launches[i] for i in sorted(launches)]
+        spacer = next((json.loads(ln).get("spacer_gb") for ln in open(log)
+                       if ln.startswith("{") and json.loads(ln).get("spacer_gb")), None)
+        spacer = "GB" if spacer is None else f"{spacer:g}"
         print("#")
         print(f"# pass {k}: " + " ".join(names))
+        print(f"#   rocprofv3 --pmc {' '.join(names)} --output-format csv -d "
+              f"$R/gpurun_out/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
+              f"$R/bench.py --placement-probe {spacer} > $R/gpurun_out/{os.path.basename(log)}"
+              " 2>&1")
         print("# placement  kind       ms  " + "  ".join(f"{c:>{max(14, len(c))}s}"
                                                       for c in names))
         for i, e in enumerate(order):
