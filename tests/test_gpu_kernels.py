@@ -260,9 +260,11 @@ def test_mx_reduce_rejects_bad_sizes(zs):
         zs.zero_shard_reduce_mx([c], [s], 1.0, g_out=g[:32])           # short g_out
 
 
-def test_shard_step_with_mxfp8_gradients(zs):
+@pytest.mark.parametrize("oneshot_min", [None, 0])
+def test_shard_step_with_mxfp8_gradients(zs, oneshot_min):
     """ShardStep over MXFP8-stored replicas, gated (clip + overflow check),
-    with one overflowing call: the oracle step on the decoded replicas."""
+    with one overflowing call: the oracle step on the decoded replicas.
+    oneshot_min=0 runs every bucket's reduce in the one-shot form."""
     import torch
     n, P = 32 * 40_009, 8
     lr, b1, b2, eps, wd, max_norm = 1e-3, 0.9, 0.999, 1e-8, 0.01, 0.05
@@ -270,7 +272,8 @@ def test_shard_step_with_mxfp8_gradients(zs):
     m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
     param = O.f32_to_bf16(master)
     st = zs.ShardStep(n, P, "mxfp8", lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd,
-                      max_norm=max_norm, check_overflow=True, bucket=32 * 10_000)
+                      max_norm=max_norm, check_overflow=True, bucket=32 * 10_000,
+                      oneshot_min=oneshot_min)
     assert st.path == "materialize"
     st.master.copy_(to_dev(master))
     st.param.copy_(to_dev(param))
@@ -773,7 +776,7 @@ def test_device_counter_matches_host_counter(zs):
 
 
 @pytest.mark.parametrize("case", ["buckets", "recompute", "fused", "oneshot"])
-def test_graph_replay_matches_eager(zs, case, monkeypatch):
+def test_graph_replay_matches_eager(zs, case):
     """One step recorded once and replayed: after every replay, with eager
     work and synchronisation between replays, the state is bitwise that of
     the same step run eagerly.  Cases: 8 bf16 replicas in 34 buckets with the
@@ -784,9 +787,8 @@ def test_graph_replay_matches_eager(zs, case, monkeypatch):
     import torch
     n = 65536 + 96
     if case == "oneshot":
-        import zero_sharded_mixed_step_amd.step as step_mod
-        monkeypatch.setattr(step_mod, "ONESHOT_MIN", 0)   # the workspace at this size too
-        P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP), 5
+        # the one-shot reduce (workspace) at this size too
+        P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, oneshot_min=0), 5
     elif case == "buckets":
         P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, bucket=32 * 61), 4
     elif case == "recompute":

@@ -73,7 +73,8 @@ class ShardStep:
                  check_overflow: bool = False, loss_scale: float = 1.0,
                  bucket: Optional[int] = None, pack: bool = False,
                  fuse_pack: bool = True, path: Optional[str] = None,
-                 device_counter: bool = False, device="cuda"):
+                 device_counter: bool = False, oneshot_min: Optional[int] = None,
+                 device="cuda"):
         self.n, self.P = int(n), int(P)
         self.lr, self.beta1, self.beta2, self.eps, self.wd = lr, beta1, beta2, eps, weight_decay
         self.max_norm, self.check_overflow = float(max_norm), bool(check_overflow)
@@ -97,10 +98,11 @@ class ShardStep:
         self.g = (torch.empty(self.n, dtype=torch.float32, device=dev)
                   if path == "materialize" else None)
         self.acc = B.new_norm_acc(1, dev)
-        # The reduce's one-shot workspace, for launches above ONESHOT_MIN
-        # elements: zeroed here, left zeroed by every reduce call (so a
-        # recorded graph replays without clearing it).
+        # The reduce's one-shot workspace, for launches above oneshot_min
+        # elements (default ONESHOT_MIN): zeroed here, left zeroed by every
+        # reduce call (so a recorded graph replays without clearing it).
         self.reduce_ws = B.new_reduce_workspace(dev)
+        self.oneshot_min = ONESHOT_MIN if oneshot_min is None else int(oneshot_min)
         self.skipped = torch.zeros(1, dtype=torch.int32, device=dev)
         self._skip_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
         self._skip_event = None
@@ -133,7 +135,7 @@ class ShardStep:
         if self.path == "fused":
             return
         for lo, hi in self._ranges():
-            ws = self.reduce_ws if hi - lo > ONESHOT_MIN else None
+            ws = self.reduce_ws if hi - lo > self.oneshot_min else None
             if self.mx_grads:
                 codes = [c[lo:hi] for c, _ in replicas]
                 scales = [sc[lo // 32:hi // 32] for _, sc in replicas]
