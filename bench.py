@@ -237,7 +237,7 @@ def step_kernels(w):
     return out
 
 
-PROFILE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_<TAG> "
+PROFILE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/<PROF_DIR> "
                "-o run -- python3 $R/bench.py --config {cfg} --steps 5 --warmup 1 "
                "--no-cpu-baseline")
 
@@ -255,13 +255,13 @@ def trace_report(w, prof_dir, bench_log):
     if line and "command" in json.loads(line):
         args = json.loads(line)["command"].split()[2:]
         cmd = cmd.split(" -- ")[0] + " -- python3 $R/bench.py" + "".join(" " + a for a in args)
-    tag = os.path.basename(os.path.normpath(prof_dir))
-    cmd = cmd.replace("prof_<TAG>", tag) + f" > $R/gpurun_out/{os.path.basename(bench_log)} 2>&1"
+    prof_rel, log_rel = os.path.normpath(prof_dir), os.path.normpath(bench_log)
+    cmd = cmd.replace("<PROF_DIR>", prof_rel) + f" > $R/{log_rel} 2>&1"
     print(f"# rocprofv3 kernel-trace summary: optimizer step, {w.name} ({w.title})")
     print("# MI355X (gfx950), one GPU.  Data (run from /tmp with TMPDIR=/tmp, repo at $R):")
     print("#   " + cmd)
-    print(f"# This summary: python bench.py --trace-report gpurun_out/{tag} "
-          f"gpurun_out/{os.path.basename(bench_log)} --config {w.name}")
+    print(f"# This summary: python bench.py --trace-report {prof_rel} {log_rel} "
+          f"--config {w.name}")
     print(f"# Pass structure: {_path_of(w)}; bucket: {w.bucket}.  Durations in ns.  The run "
           "also times the unfused chain (unfused_kernel<..>, gate_kernel, and")
     print("# shard_reduce_kernel / mxfp8_kernel launches of the chain); fill_kernel is the "
@@ -294,13 +294,18 @@ def traffic_report(names):
     print(f"# MI355X (gfx950), one GPU.  Kernel sources digest: {', '.join(digests)}")
     print("# Counter runs (each its own process, from /tmp with TMPDIR=/tmp, repo at $R), "
           "for CTR in FETCH_SIZE WRITE_SIZE:")
-    print("#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/pmc_copy_$CTR -o run "
+    def counter_dir(cmd, i):
+        # the i-th directory argument of a recorded --summarize-pmc command,
+        # without its _FETCH_SIZE / _WRITE_SIZE suffix
+        args = cmd.split()
+        d = args[args.index("--summarize-pmc") + 1 + i]
+        return d.rsplit("_", 2)[0] if d.endswith("_SIZE") else d
+    first = data[names[0]]["command"]
+    print(f"#   rocprofv3 --pmc $CTR --output-format csv -d $R/{counter_dir(first, 2)}_$CTR -o run "
           "-- python3 $R/bench.py --copy-calibration")
-    import re
     for n in names:
-        m = re.search(r"gpurun_out/(pmc_\w+?)_FETCH_SIZE", data[n]["command"])
-        tag = m.group(1) if m else "pmc_<TAG>"
-        print(f"#   rocprofv3 --pmc $CTR --output-format csv -d $R/gpurun_out/{tag}_$CTR -o run "
+        print(f"#   rocprofv3 --pmc $CTR --output-format csv -d "
+              f"$R/{counter_dir(data[n]['command'], 0)}_$CTR -o run "
               f"-- python3 $R/bench.py --config {n} --steps 2 --warmup 1 --no-cpu-baseline "
               "--no-unfused")
     print("# Scaled (no GPU), the commands recorded in profiles/hbm_traffic.json:")
@@ -348,8 +353,8 @@ def placement_report(pairs):
           "(bench.py --placement-probe GB).")
     print("# MI355X (gfx950), one GPU.  One counter pass per run (its own process, from /tmp "
           "with TMPDIR=/tmp, repo at $R); each pass below gives its command.")
-    print("# This summary (from gpurun_out): python bench.py --placement-report " + " ".join(
-        f"{os.path.basename(os.path.normpath(d))} {os.path.basename(lg)}" for d, lg in runs))
+    print("# This summary: python bench.py --placement-report " + " ".join(
+        f"{os.path.normpath(d)} {os.path.normpath(lg)}" for d, lg in runs))
     print("# Launch durations (ms) are rocprofv3's per-dispatch timestamps under counter "
           "collection.  TCC_EA0 DRAM read requests are 128 B, write requests 64 B; GMI = "
           "inter-die.")
@@ -376,8 +381,8 @@ def placement_report(pairs):
         print("#")
         print(f"# pass {k}: " + " ".join(names))
         print(f"#   rocprofv3 --pmc {' '.join(names)} --output-format csv -d "
-              f"$R/gpurun_out/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
-              f"$R/bench.py --placement-probe {spacer} > $R/gpurun_out/{os.path.basename(log)}"
+              f"$R/{os.path.normpath(d)} -o run -- python3 "
+              f"$R/bench.py --placement-probe {spacer} > $R/{os.path.normpath(log)}"
               " 2>&1")
         print("# placement  kind       ms  " + "  ".join(f"{c:>{max(14, len(c))}s}"
                                                       for c in names))
