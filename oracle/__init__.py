@@ -25,14 +25,16 @@ class Scalars(C.Structure):
                 ("b1", "b2", "omb1", "omb2", "step_size", "sqrt_bc2", "decay", "eps")]
 
 
+ACC_WORDS = 16
+
+
 class Acc(C.Structure):
-    """Exact sum of squares: X * 2^-128, X held in 8 little-endian u32 digits."""
-    _fields_ = [("w", C.c_uint32 * 8), ("nonfinite", C.c_uint64),
-                ("overflow", C.c_uint64)]
+    """Exact sum of squares: X * 2^-128, X held in 16 little-endian u32 digits."""
+    _fields_ = [("w", C.c_uint32 * ACC_WORDS), ("nonfinite", C.c_uint64)]
 
     @property
     def X(self) -> int:
-        return sum(int(self.w[k]) << (32 * k) for k in range(8))
+        return sum(int(self.w[k]) << (32 * k) for k in range(ACC_WORDS))
 
     def copy(self) -> "Acc":
         out = Acc()
@@ -80,6 +82,8 @@ def _load(path):
     L.oracle_acc_sumsq.restype = C.c_double
     L.oracle_clip_coef.argtypes = [C.c_double, C.c_double]
     L.oracle_clip_coef.restype = C.c_float
+    L.oracle_gate.argtypes = [C.POINTER(Acc), C.c_double, C.c_int, C.POINTER(C.c_float)]
+    L.oracle_gate.restype = C.c_int
     L.oracle_adamw.argtypes = [sz, vp, C.c_float, C.POINTER(Scalars), vp, vp, vp, vp]
     L.oracle_step.argtypes = [C.POINTER(vp), C.c_int, C.c_int, sz, C.c_float,
                               C.c_double, C.c_int] + [C.c_double] * 5 + [
@@ -195,6 +199,14 @@ def clip_coef(sumsq: float, max_norm: float) -> float:
     return lib().oracle_clip_coef(float(sumsq), float(max_norm))
 
 
+def gate(acc: Acc, max_norm: float, check_overflow: bool):
+    """(skip, coef) of a step from its global accumulator (oracle_gate)."""
+    coef = C.c_float()
+    skip = lib().oracle_gate(C.byref(acc), float(max_norm), int(bool(check_overflow)),
+                             C.byref(coef))
+    return bool(skip), coef.value
+
+
 # ----------------------------------------------------------------- AdamW ---
 
 def adamw(g, coef, s: Scalars, master, m, v, param=None):
@@ -259,9 +271,9 @@ def step_parallel(replicas, inv_scale_f, max_norm, check_overflow, lr, beta1, be
         own = acc_zero()
         for part in parts:
             acc_add(own, part)
-        if check_overflow and (own.nonfinite + own.overflow) > 0:
+        skip, coef = gate(own, max_norm, check_overflow)
+        if skip:
             return True, own
-        coef = clip_coef(acc_sumsq(own), max_norm)
         s = make_scalars(lr, beta1, beta2, eps, wd, t)
 
         def second(c):

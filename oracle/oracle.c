@@ -117,11 +117,13 @@ void oracle_reduce(const void *const *replicas, int P, int dtype, size_t n,
 
 void oracle_acc_zero(oracle_acc *acc) { memset(acc, 0, sizeof(*acc)); }
 
-/* X += 2^pos, pos in [0, 256). */
-static void big_add_pow2(uint32_t w[8], int pos) {
+#define ACC_WORDS 16 /* 512 bits */
+
+/* X += 2^pos, pos in [0, 512). */
+static void big_add_pow2(uint32_t w[ACC_WORDS], int pos) {
   int k = pos / 32;
   uint64_t carry = (uint64_t)1 << (pos % 32);
-  while (carry != 0 && k < 8) {
+  while (carry != 0 && k < ACC_WORDS) {
     uint64_t t = (uint64_t)w[k] + carry;
     w[k] = (uint32_t)t;
     carry = t >> 32;
@@ -131,13 +133,12 @@ static void big_add_pow2(uint32_t w[8], int pos) {
 
 void oracle_acc_add(oracle_acc *dst, const oracle_acc *src) {
   uint64_t carry = 0;
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < ACC_WORDS; ++k) {
     uint64_t t = (uint64_t)dst->w[k] + src->w[k] + carry;
     dst->w[k] = (uint32_t)t;
     carry = t >> 32;
   }
   dst->nonfinite += src->nonfinite;
-  dst->overflow += src->overflow;
 }
 
 void oracle_acc_add_fixed(oracle_acc *acc, double S) {
@@ -158,7 +159,6 @@ void oracle_acc_add_fixed(oracle_acc *acc, double S) {
 }
 
 void oracle_norm_accumulate(const float *g, size_t n, oracle_acc *acc) {
-  const double two64 = 18446744073709551616.0; /* 2^64 */
   for (size_t gs = 0; gs < n; gs += 32) {
     double a[4];
     for (int j = 0; j < 4; ++j) {
@@ -180,21 +180,18 @@ void oracle_norm_accumulate(const float *g, size_t n, oracle_acc *acc) {
       a[j] = sum;
     }
     double S = (a[0] + a[1]) + (a[2] + a[3]);
-    if (S >= two64)
-      acc->overflow += 1;
-    else
-      oracle_acc_add_fixed(acc, S);
+    oracle_acc_add_fixed(acc, S);
   }
 }
 
-static int big_bit(const uint32_t w[8], int pos) {
+static int big_bit(const uint32_t w[ACC_WORDS], int pos) {
   if (pos < 0) return 0;
   return (int)((w[pos / 32] >> (pos % 32)) & 1u);
 }
 
 double oracle_acc_sumsq(const oracle_acc *acc) {
   int top = -1;
-  for (int pos = 255; pos >= 0; --pos) {
+  for (int pos = 32 * ACC_WORDS - 1; pos >= 0; --pos) {
     if (big_bit(acc->w, pos)) {
       top = pos;
       break;
@@ -225,6 +222,19 @@ float oracle_clip_coef(double sumsq, double max_norm) {
   double denom = norm + 1e-6;
   double c = max_norm / denom;
   return (c < 1.0) ? (float)c : 1.0f;
+}
+
+int oracle_gate(const oracle_acc *acc, double max_norm, int check_overflow,
+                float *coef) {
+  *coef = 1.0f;
+  if (check_overflow && acc->nonfinite > 0) return 1;
+  if (max_norm > 0.0) {
+    if (acc->nonfinite > 0)
+      *coef = 0.0f;
+    else
+      *coef = oracle_clip_coef(oracle_acc_sumsq(acc), max_norm);
+  }
+  return 0;
 }
 
 /* --------------------------------------------------------------- AdamW -- */
@@ -264,8 +274,8 @@ int oracle_step(const void *const *replicas, int P, int dtype, size_t n,
   if (acc_out) *acc_out = own;
   global = own;
   for (int k = 0; k < n_extra; ++k) oracle_acc_add(&global, &extra[k]);
-  if (check_overflow && (global.nonfinite + global.overflow) > 0) return 1;
-  float coef = oracle_clip_coef(oracle_acc_sumsq(&global), max_norm);
+  float coef;
+  if (oracle_gate(&global, max_norm, check_overflow, &coef)) return 1;
   oracle_scalars s;
   oracle_make_scalars(lr, beta1, beta2, eps, wd, step, &s);
   oracle_adamw(n, g_tmp, coef, &s, master, m, v, param);

@@ -72,30 +72,38 @@ void oracle_reduce(const void *const *replicas, int P, int dtype, size_t n,
 
 /* Exact global sum of squares.  X is a non-negative integer, the value of
  * the sum is X * 2^-128.  w[] holds X in 32-bit digits, least significant
- * first, always carry-normalised. */
+ * first, always carry-normalised.  512 bits hold the sum of up to 2^32
+ * groups, each below 2^(261+128): every finite binary32 gradient counts. */
 typedef struct {
-  uint32_t w[8];
+  uint32_t w[16];
   uint64_t nonfinite;
-  uint64_t overflow;
 } oracle_acc;
 
 void oracle_acc_zero(oracle_acc *acc);
 void oracle_acc_add(oracle_acc *dst, const oracle_acc *src);
-/* Adds floor(S * 2^128) for one non-negative binary64 S < 2^64. */
+/* Adds floor(S * 2^128) for one finite, non-negative binary64 S < 2^262. */
 void oracle_acc_add_fixed(oracle_acc *acc, double S);
 /* The norm contribution of g[0..n): groups of 32 elements aligned to g[0]
  * (a short last group is padded with +0).  In a group, q_i = g_i*g_i in
  * binary64 (exact), a_j = q_{8j} + ... + q_{8j+7} summed left to right,
  * S = (a_0 + a_1) + (a_2 + a_3); non-finite g_i count in `nonfinite` and
- * give q_i = 0; S >= 2^64 counts in `overflow` and adds nothing; otherwise
- * floor(S * 2^128) is added to X exactly. */
+ * give q_i = 0; floor(S * 2^128) is added to X exactly (S < 2^261 for
+ * finite binary32 inputs, so no group is left out). */
 void oracle_norm_accumulate(const float *g, size_t n, oracle_acc *acc);
 /* RNE_binary64(X * 2^-128). */
 double oracle_acc_sumsq(const oracle_acc *acc);
-/* Global-norm clip coefficient: 1.0f if max_norm <= 0; otherwise
- * c = max_norm / (sqrt(sumsq) + 1e-6) in binary64 and coef = c < 1 ? f32(c)
- * : 1.0f. */
+/* Global-norm clip coefficient of a finite norm: 1.0f if max_norm <= 0;
+ * otherwise c = max_norm / (sqrt(sumsq) + 1e-6) in binary64 and
+ * coef = c < 1 ? f32(c) : 1.0f. */
 float oracle_clip_coef(double sumsq, double max_norm);
+/* The step's gate from the global accumulator.  Returns 1 (skip: nothing is
+ * written, t is not advanced) when check_overflow is set and nonfinite > 0.
+ * Otherwise returns 0 and sets *coef: 1.0f when max_norm <= 0; 0.0f when
+ * max_norm > 0 and nonfinite > 0 (a non-finite element makes the global
+ * norm infinite, and max_norm / (inf + 1e-6) = 0); else
+ * oracle_clip_coef(oracle_acc_sumsq(acc), max_norm). */
+int oracle_gate(const oracle_acc *acc, double max_norm, int check_overflow,
+                float *coef);
 
 /* Fused AdamW on n elements, in place, per element in binary32:
  *   g' = g * coef
@@ -111,9 +119,9 @@ void oracle_adamw(size_t n, const float *g, float coef, const oracle_scalars *s,
 
 /* One whole step of one rank: reduce + average of the replicas into g_tmp
  * (caller scratch, n floats), its norm accumulator, plus `n_extra` accs of
- * the other ranks (the all-reduce of the 64-byte norm state), the skip gate
- * (check_overflow and nonfinite+overflow > 0 -> nothing written, returns 1),
- * the clip coefficient, then AdamW with t = step.  Returns 0 when applied.
+ * the other ranks (the all-reduce of the norm state), the gate
+ * (oracle_gate: a skip writes nothing and returns 1), then AdamW with
+ * t = step and the gate's coefficient.  Returns 0 when applied.
  * acc_out (nullable) receives this rank's own accumulator. */
 int oracle_step(const void *const *replicas, int P, int dtype, size_t n,
                 float inv_scale, double max_norm, int check_overflow,

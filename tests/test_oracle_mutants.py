@@ -49,7 +49,17 @@ MUTANTS = [
     ("clip_without_sqrt", "double norm = sqrt(sumsq);", "double norm = sumsq;"),
     ("clip_no_clamp", "return (c < 1.0) ? (float)c : 1.0f;", "return (float)c;"),
     ("clip_no_eps", "double denom = norm + 1e-6;", "double denom = norm;"),
-    ("skip_ignores_overflow", "(global.nonfinite + global.overflow) > 0", "global.nonfinite > 0"),
+    ("gate_skips_without_check", "if (check_overflow && acc->nonfinite > 0) return 1;",
+     "if (acc->nonfinite > 0) return 1;"),
+    ("gate_clip_ignores_nonfinite", "    if (acc->nonfinite > 0)\n      *coef = 0.0f;\n    else\n      *coef",
+     "    if (0)\n      *coef = 0.0f;\n    else\n      *coef"),
+    ("norm_drops_large_groups", "    oracle_acc_add_fixed(acc, S);\n  }\n}",
+     "    if (S < 18446744073709551616.0) oracle_acc_add_fixed(acc, S);\n  }\n}"),
+    ("acc_narrow_256_bits", "while (carry != 0 && k < ACC_WORDS) {", "while (carry != 0 && k < 8) {"),
+    ("u_by_reciprocal", "float u = mi / d;", "float u = mi * (1.0f / d);"),
+    ("m_mul_then_add", "float mi = fmaf(s->b1, m[i], t1);", "float mi = s->b1 * m[i] + t1;"),
+    ("v_mul_then_add", "float vi = fmaf(s->b2, v[i], t3);", "float vi = s->b2 * v[i] + t3;"),
+    ("update_mul_then_add", "th = fmaf(-s->step_size, u, th);", "th = -s->step_size * u + th;"),
     ("other_ranks_ignored", "for (int k = 0; k < n_extra; ++k) oracle_acc_add",
      "for (int k = 0; k < 0; ++k) oracle_acc_add"),
     ("bf16_ties_up", "up = (lo_mag & 1u) ? 1 : 0; /* tie", "up = 1; /* tie"),
