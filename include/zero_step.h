@@ -35,12 +35,17 @@
  *     kernels were launched.  Faults inside them surface at the caller's next
  *     synchronisation.
  *   - The caller owns every buffer.  The library allocates nothing, never
- *     synchronises, keeps no state between calls other than a cache of each
- *     device's compute-unit count, and lets no C++ exception escape.
- *   - Device pointers must be 16-byte aligned (ZERO_EALIGN otherwise).
+ *     synchronises, keeps no state between calls, and lets no C++ exception
+ *     escape.
+ *   - Alignment (ZERO_EALIGN otherwise): every device array and every
+ *     zero_norm_acc must be 16-byte aligned; the exceptions are the
+ *     per-block scale bytes of MXFP8-stored replicas (any alignment), the
+ *     int32/float scalar outputs (4 bytes) and the int64 step counter (8).
  *     Outputs must not overlap inputs, except master/m/v, which are updated
  *     in place.
  *   - Element counts are size_t; n == 0 is a valid no-op returning ZERO_OK.
+ *     A call that adds to a norm accumulator takes n <= 2^37 (ZERO_ESIZE
+ *     beyond): that is the accumulator's capacity.
  *   - Arithmetic is IEEE binary32/binary64 with round to nearest even and
  *     denormals kept; every sum runs in one fixed order, so results are
  *     bitwise reproducible and independent of grid shape.
@@ -55,12 +60,12 @@
 extern "C" {
 #endif
 
-#define ZERO_ABI_VERSION 4
+#define ZERO_ABI_VERSION 5
 #define ZERO_MAX_REPLICAS 64
 
 /* Element types of gradient replicas.  ZERO_MXFP8 replicas (E4M3 codes plus
  * one E8M0 scale byte per 32 elements) are accepted by zero_shard_reduce_mx
- * only. */
+ * and zero_shard_reduce_mx_ws only. */
 enum { ZERO_F32 = 0, ZERO_BF16 = 1, ZERO_MXFP8 = 2 };
 
 /* Status codes. */
@@ -68,52 +73,54 @@ enum {
   ZERO_OK = 0,
   ZERO_EINVAL = -1, /* null required pointer, P outside [1,64], bad dtype,
                        step < 1, conflicting or missing gradient source */
-  ZERO_EALIGN = -2, /* a device pointer is not 16-byte aligned */
-  ZERO_ESIZE = -3,  /* MXFP8 pack with n % 32 != 0, n >= 2^32 in a call
+  ZERO_EALIGN = -2, /* a pointer breaks the alignment rule above */
+  ZERO_ESIZE = -3,  /* MXFP8 pack with n % 32 != 0, n > 2^37 in a call
                        that adds to a norm accumulator, or a workspace below
                        ZERO_REDUCE_WORKSPACE_BYTES */
   ZERO_EHIP = -4    /* the HIP runtime reported a launch error */
 };
 
 /* Exact, order-independent sum of squares of a gradient, plus its count of
- * non-finite values.  64 bytes in device memory, 8-byte aligned; the caller
- * zeroes it (zero_norm_acc_clear) before the first call that adds to it.
+ * non-finite values.  128 bytes in device memory, 16-byte aligned; the
+ * caller zeroes it (zero_norm_acc_clear) before the first call that adds to
+ * it.
  *
  * The sum is X * 2^-128 with the non-negative integer
- *   X = sum_k digit[k] * 2^(32k)            (k = 0..6; carries pending).
+ *   X = sum_k digit[k] * 2^(32k)            (k = 0..12; carries pending).
  * Each call splits its range into 32-element groups aligned to the range
  * start (a short last group is padded with +0).  Per group, with g the
  * averaged, unscaled gradient in binary32 and q_i = g_i^2 in binary64
  * (exact), a_j = q_{8j} + ... + q_{8j+7} summed left to right and
  * S = (a_0 + a_1) + (a_2 + a_3); floor(S * 2^128) is added to X exactly.
- * A non-finite g_i counts in `nonfinite` and adds 0; a group with S >= 2^64
- * counts in `overflow` and adds nothing.  Integer addition makes X the same
- * for any grid, bucket split or rank order, and accumulators of different
- * ranks or buckets combine by adding their fields (the 64-byte all-reduce of
- * a multi-GPU run).  Capacity: at most 2^37 elements in total per
- * accumulator (2^32 groups, so no digit wraps); the two counts are kept
- * modulo 2^32. */
+ * A non-finite g_i counts in `nonfinite` and adds 0.  Every finite group
+ * counts: S < 2^261 for finite binary32 values, so floor(S * 2^128) < 2^389
+ * fits the 13 digits, each of which receives one piece below 2^32 per
+ * group.  Integer addition makes X the same for any grid, bucket split or
+ * rank order, and accumulators of different ranks or buckets combine by
+ * adding their fields (the norm all-reduce of a multi-GPU run).  Capacity:
+ * at most 2^37 elements in total per accumulator (2^32 groups, so no digit
+ * wraps).  reserved[] stays zero. */
 typedef struct zero_norm_acc {
-  uint64_t digit[7];
-  uint32_t nonfinite;
-  uint32_t overflow;
+  uint64_t digit[13];
+  uint64_t nonfinite;
+  uint64_t reserved[2];
 } zero_norm_acc;
 
-/* Optional workspace of zero_shard_reduce and zero_shard_reduce_mx: 512
- * accumulator slots.  With one, the reduce of 4 or more replicas runs on a
+/* Workspace of zero_shard_reduce_ws and zero_shard_reduce_mx_ws: 512
+ * accumulator slots.  The reduce of 4 or more replicas then runs on a
  * one-shot grid (a few tiles per workgroup, in address order) whose
  * workgroups add their norm state to the slots, and a one-workgroup kernel
  * launched after it adds the slots to `acc` and zeroes them again.  Results
- * are bitwise the same with and without it.  Measured on MI355X it pays for
- * whole multi-GB shards; for bucket-sized calls (25e6 elements) the extra
- * launch made it slower, so pass NULL there.  Device memory of at least
+ * are bitwise those of the workspace-free call.  Measured on MI355X it pays
+ * for whole multi-GB shards; for bucket-sized calls (25e6 elements) the
+ * extra launch made it slower.  Device memory of at least
  * ZERO_REDUCE_WORKSPACE_BYTES, 16-byte aligned, zeroed by the caller before
  * its first use (zero_norm_acc_clear on it as ZERO_REDUCE_WORKSPACE_BYTES /
- * 64 accumulators does that) and left zeroed by every call that returns
+ * 128 accumulators does that) and left zeroed by every call that returns
  * ZERO_OK; after any other status, zero it again before reusing it.  Calls
  * that share a workspace must not run concurrently (order them on one
  * stream). */
-#define ZERO_REDUCE_WORKSPACE_BYTES (64 * 512)
+#define ZERO_REDUCE_WORKSPACE_BYTES (128 * 512)
 
 /* Zero n_accs accumulators with a fill kernel (safe inside stream capture). */
 int zero_norm_acc_clear(zero_norm_acc *accs, int n_accs, void *stream);
@@ -124,18 +131,22 @@ float zero_inv_scale(int P, double loss_scale);
 
 /* Shard reduce: g[i] = (r_0[i] + r_1[i] + ... + r_{P-1}[i]) * inv_scale,
  * summed in binary32 in rank order 0..P-1 (the reduce half of
- * reduce-scatter, then the data-parallel average).
+ * reduce-scatter, then the data-parallel average), plus the norm state of g.
  *   replicas  HOST array of P device pointers; replicas[k] is rank k's copy
  *             of the same n elements (for a bucket, the same offset into
  *             each replica).  dtype ZERO_F32 or ZERO_BF16.
  *   g_out     device fp32[n], or NULL to skip writing the averaged gradient.
  *   acc       device accumulator to add this range's norm state to, or NULL.
- *   workspace device workspace (ZERO_REDUCE_WORKSPACE_BYTES above) or NULL;
- *             workspace_bytes its size (ZERO_ESIZE if too small).
  * At least one of g_out and acc must be given. */
 int zero_shard_reduce(const void *const *replicas, int P, int dtype, size_t n,
-                      float inv_scale, float *g_out, zero_norm_acc *acc,
-                      void *workspace, size_t workspace_bytes, void *stream);
+                      float inv_scale, float *g_out, zero_norm_acc *acc, void *stream);
+
+/* The same reduce with a caller-owned workspace (ZERO_REDUCE_WORKSPACE_BYTES
+ * above; workspace_bytes its size, ZERO_ESIZE if too small): the one-shot
+ * form for whole shards.  Bitwise the same results. */
+int zero_shard_reduce_ws(const void *const *replicas, int P, int dtype, size_t n,
+                         float inv_scale, float *g_out, zero_norm_acc *acc,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Shard reduce of MXFP8-stored gradient replicas (the "12 percent off stored
  * state" of Zero_From_Scratch's outline item on MXFP8: bf16 gradients kept
@@ -150,12 +161,15 @@ int zero_shard_reduce(const void *const *replicas, int P, int dtype, size_t n,
  *   scales[k]  HOST array of P device pointers to uint8[n/32] scale bytes
  *              (any alignment); for a bucket at element offset `lo` pass
  *              codes + lo and scales + lo/32.
- *   n % 32 == 0 (ZERO_ESIZE otherwise).  g_out / acc / workspace as
- *   zero_shard_reduce. */
+ *   n % 32 == 0 (ZERO_ESIZE otherwise).  g_out / acc as zero_shard_reduce;
+ *   the _ws form takes a workspace as zero_shard_reduce_ws. */
 int zero_shard_reduce_mx(const uint8_t *const *codes, const uint8_t *const *scales,
                          int P, size_t n, float inv_scale, float *g_out,
-                         zero_norm_acc *acc, void *workspace, size_t workspace_bytes,
-                         void *stream);
+                         zero_norm_acc *acc, void *stream);
+int zero_shard_reduce_mx_ws(const uint8_t *const *codes, const uint8_t *const *scales,
+                            int P, size_t n, float inv_scale, float *g_out,
+                            zero_norm_acc *acc, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Norm state of one buffer: adds the groups of g[i] = grad[i] * inv_scale
  * (grad fp32 or bf16, device) to acc, as zero_shard_reduce with P = 1 and
@@ -198,11 +212,13 @@ typedef struct zero_adamw_args {
 
 /* Fused AdamW step on n elements of fp32 master/m/v.
  * Gate (evaluated on the device from the accumulators, no host sync):
- *   nonfinite + overflow summed over accs > 0 and check_overflow -> nothing
- *   is written and *skipped_out = 1 (the caller then keeps `step`);
- *   otherwise sumsq = RNE_binary64(X * 2^-128),
- *   coef = 1 if max_norm <= 0, else c = max_norm / (sqrt(sumsq) + 1e-6) in
- *   binary64 and coef = c < 1 ? f32(c) : 1.
+ *   nonfinite summed over accs > 0 and check_overflow -> nothing is written
+ *   and *skipped_out = 1 (the caller then keeps `step`); otherwise
+ *   coef = 1 if max_norm <= 0;
+ *   coef = 0 if max_norm > 0 and nonfinite > 0 (a non-finite element makes
+ *   the global norm infinite: max_norm / (inf + 1e-6) = 0);
+ *   else sumsq = RNE_binary64(X * 2^-128), c = max_norm / (sqrt(sumsq) +
+ *   1e-6) in binary64 and coef = c < 1 ? f32(c) : 1.
  * Scalars (binary64, each rounded once to binary32): b1 = f32(beta1),
  *   b2 = f32(beta2), omb1 = f32(1 - beta1), omb2 = f32(1 - beta2),
  *   beta^t by square-and-multiply over the bits of t from the least

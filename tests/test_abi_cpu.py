@@ -45,11 +45,43 @@ def test_binding_constants_match_the_header():
     assert int(consts["ZERO_MAX_REPLICAS"]) == B.ZERO_MAX_REPLICAS
     a, b = re.fullmatch(r"\((\d+) \* (\d+)\)", consts["ZERO_REDUCE_WORKSPACE_BYTES"]).groups()
     assert int(a) * int(b) == B.REDUCE_WORKSPACE_BYTES
+    assert int(a) == 8 * B.ACC_WORDS                      # one slot = one zero_norm_acc
+    body = re.search(r"typedef struct zero_norm_acc \{(.*?)\} zero_norm_acc;", text, re.S).group(1)
+    fields = re.findall(r"uint64_t (\w+)(?:\[(\d+)\])?;", body)
+    assert fields == [("digit", str(B.ACC_DIGITS)), ("nonfinite", ""), ("reserved", "2")]
+    assert sum(int(k or 1) for _, k in fields) == B.ACC_WORDS
+
+
+def _prototype(text, name):
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"\bint\s+" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = [" ".join(p.split()) for p in m.group(1).split(",")]
+    return [re.sub(r"\s*\*\s*", "* ", p).replace("* ", "*").strip() for p in params]
+
+
+def test_path_calls_have_the_specified_signatures():
+    """The four calls of the path, parameter by parameter: plain pointers and
+    sizes, the stream last (void* stands for hipStream_t in this C header)."""
+    text = open(HEADER).read()
+    want = {
+        "zero_shard_reduce": ["const void *const *replicas", "int P", "int dtype", "size_t n",
+                              "float inv_scale", "float *g_out", "zero_norm_acc *acc",
+                              "void *stream"],
+        "zero_grad_norm": ["const void *grad", "int dtype", "size_t n", "float inv_scale",
+                           "zero_norm_acc *acc", "void *stream"],
+        "zero_adamw_step": ["const zero_adamw_args *args", "void *stream"],
+        "zero_mxfp8_pack": ["const uint16_t *bf16_in", "size_t n", "uint8_t *elem_out",
+                            "uint8_t *scale_out", "void *stream"],
+    }
+    norm = lambda ps: [re.sub(r"\s*\*\s*", "*", p) for p in ps]
+    for name, params in want.items():
+        assert norm(_prototype(text, name)) == norm(params), name
 
 
 def test_version_and_status_strings(lib):
     lib.zero_abi_version.restype = C.c_int
-    assert lib.zero_abi_version() == 4
+    assert lib.zero_abi_version() == 5
     lib.zero_strerror.restype = C.c_char_p
     lib.zero_strerror.argtypes = [C.c_int]
     texts = {lib.zero_strerror(s).decode() for s in (0, -1, -2, -3, -4, 7)}
@@ -65,40 +97,55 @@ def test_inv_scale_matches_definition(lib):
 
 
 def test_argument_checks(lib):
-    vp = C.c_void_p
-    lib.zero_shard_reduce.argtypes = [vp, C.c_int, C.c_int, C.c_size_t, C.c_float, vp, vp, vp,
-                                      C.c_size_t, vp]
-    lib.zero_shard_reduce_mx.argtypes = [vp, vp, C.c_int, C.c_size_t, C.c_float, vp, vp, vp,
-                                         C.c_size_t, vp]
-    lib.zero_mxfp8_pack.argtypes = [vp, C.c_size_t, vp, vp, vp]
-    lib.zero_grad_norm.argtypes = [vp, C.c_int, C.c_size_t, C.c_float, vp, vp]
+    """Every case fails its checks or is a zero-length no-op, so nothing is
+    launched.  Alignment: 16 bytes for device arrays and accumulators, any for
+    MXFP8 scale bytes, 4 for int32/float outputs, 8 for the step counter."""
+    vp, sz, i, f = C.c_void_p, C.c_size_t, C.c_int, C.c_float
+    lib.zero_shard_reduce.argtypes = [vp, i, i, sz, f, vp, vp, vp]
+    lib.zero_shard_reduce_ws.argtypes = [vp, i, i, sz, f, vp, vp, vp, sz, vp]
+    lib.zero_shard_reduce_mx.argtypes = [vp, vp, i, sz, f, vp, vp, vp]
+    lib.zero_shard_reduce_mx_ws.argtypes = [vp, vp, i, sz, f, vp, vp, vp, sz, vp]
+    lib.zero_mxfp8_pack.argtypes = [vp, sz, vp, vp, vp]
+    lib.zero_grad_norm.argtypes = [vp, i, sz, f, vp, vp]
     lib.zero_adamw_step.argtypes = [vp, vp]
-    lib.zero_norm_acc_clear.argtypes = [vp, C.c_int, vp]
+    lib.zero_norm_acc_clear.argtypes = [vp, i, vp]
+    lib.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
     fake = 0x10000                     # aligned, never dereferenced
     reps = (vp * 2)(fake, fake + 0x1000)
-    assert lib.zero_shard_reduce(None, 2, 1, 64, 1.0, fake, None, None, 0, None) == -1
-    assert lib.zero_shard_reduce(reps, 0, 1, 64, 1.0, fake, None, None, 0, None) == -1
-    assert lib.zero_shard_reduce(reps, 65, 1, 64, 1.0, fake, None, None, 0, None) == -1
-    assert lib.zero_shard_reduce(reps, 2, 5, 64, 1.0, fake, None, None, 0, None) == -1
-    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, None, None, None, 0, None) == -1
-    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake + 4, None, None, 0, None) == -2
+    red = lib.zero_shard_reduce
+    assert red(None, 2, 1, 64, 1.0, fake, None, None) == -1
+    assert red(reps, 0, 1, 64, 1.0, fake, None, None) == -1
+    assert red(reps, 65, 1, 64, 1.0, fake, None, None) == -1
+    assert red(reps, 2, 5, 64, 1.0, fake, None, None) == -1
+    assert red(reps, 2, 1, 64, 1.0, None, None, None) == -1
+    assert red(reps, 2, 1, 64, 1.0, fake + 4, None, None) == -2
+    assert red(reps, 2, 1, 64, 1.0, None, fake + 8, None) == -2     # accumulator: 16 bytes
     bad = (vp * 2)(fake, fake + 2)
-    assert lib.zero_shard_reduce(bad, 2, 1, 64, 1.0, fake, None, None, 0, None) == -2
-    assert lib.zero_shard_reduce(reps, 2, 1, 1 << 32, 1.0, None, fake, None, 0, None) == -3
-    assert lib.zero_shard_reduce(reps, 2, 1, 0, 1.0, fake, None, None, 0, None) == 0
-    # the optional reduce workspace: 16-byte aligned, at least
-    # ZERO_REDUCE_WORKSPACE_BYTES (64 * 512)
-    ws = 64 * 512
-    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake, None, fake + 8, ws, None) == -2
-    assert lib.zero_shard_reduce(reps, 2, 1, 64, 1.0, fake, None, fake, ws - 1, None) == -3
-    assert lib.zero_shard_reduce(reps, 2, 1, 0, 1.0, fake, fake, fake, ws, None) == 0
-    scales = (vp * 2)(fake + 1, fake + 3)
-    assert lib.zero_shard_reduce_mx(reps, scales, 2, 64, 1.0, fake, None, fake + 8, ws,
-                                    None) == -2
-    assert lib.zero_shard_reduce_mx(reps, scales, 2, 64, 1.0, fake, None, fake, 64,
-                                    None) == -3
-    assert lib.zero_shard_reduce_mx(reps, scales, 2, 0, 1.0, fake, None, fake, ws, None) == 0
+    assert red(bad, 2, 1, 64, 1.0, fake, None, None) == -2
+    # a norm call takes up to 2^37 elements (the accumulator's capacity)
+    assert red(reps, 2, 1, (1 << 37) + 32, 1.0, None, fake, None) == -3
+    assert red(reps, 2, 1, 0, 1.0, fake, None, None) == 0
+    assert red(reps, 2, 1, 0, 1.0, fake, fake, None) == 0
+    # the workspace form: 16-byte aligned, at least ZERO_REDUCE_WORKSPACE_BYTES
+    ws = 128 * 512
+    rws = lib.zero_shard_reduce_ws
+    assert rws(reps, 2, 1, 64, 1.0, fake, None, fake + 8, ws, None) == -2
+    assert rws(reps, 2, 1, 64, 1.0, fake, None, fake, ws - 1, None) == -3
+    assert rws(reps, 2, 1, 64, 1.0, fake, None, None, ws, None) == -1   # no workspace
+    assert rws(reps, 2, 1, 0, 1.0, fake, fake, fake, ws, None) == 0
+    scales = (vp * 2)(fake + 1, fake + 3)                            # scale bytes: any
+    mx, mxws = lib.zero_shard_reduce_mx, lib.zero_shard_reduce_mx_ws
+    assert mx(reps, scales, 2, 48, 1.0, fake, None, None) == -3     # n % 32
+    assert mx(reps, scales, 2, (1 << 37) + 32, 1.0, None, fake, None) == -3
+    assert mx(bad, scales, 2, 64, 1.0, fake, None, None) == -2
+    assert mx(reps, scales, 2, 0, 1.0, fake, None, None) == 0
+    assert mxws(reps, scales, 2, 64, 1.0, fake, None, fake + 8, ws, None) == -2
+    assert mxws(reps, scales, 2, 64, 1.0, fake, None, fake, 64, None) == -3
+    assert mxws(reps, scales, 2, 0, 1.0, fake, None, fake, ws, None) == 0
+    assert mxws(reps, scales, 2, 64, 1.0, fake, None, None, ws, None) == -1
     assert lib.zero_grad_norm(None, 1, 64, 1.0, fake, None) == -1
+    assert lib.zero_grad_norm(fake, 1, 64, 1.0, fake + 8, None) == -2
+    assert lib.zero_grad_norm(fake, 1, (1 << 37) + 1, 1.0, fake, None) == -3
     assert lib.zero_mxfp8_pack(fake, 33, fake, fake, None) == -3
     assert lib.zero_mxfp8_pack(fake, 64, fake, fake + 1, None) == -2
     assert lib.zero_mxfp8_pack(None, 64, fake, fake, None) == -1
@@ -107,9 +154,12 @@ def test_argument_checks(lib):
     assert lib.zero_norm_acc_clear(None, 1, None) == -1
     assert lib.zero_norm_acc_clear(fake + 8, 1, None) == -2
     assert lib.zero_norm_acc_clear(None, 0, None) == 0
+    assert lib.zero_step_gate(fake + 8, 1, 1.0, 1, fake, fake, None) == -2
+    assert lib.zero_step_gate(fake, 1, 1.0, 1, fake + 2, fake, None) == -2
+    assert lib.zero_step_gate(fake, 1, 1.0, 1, None, fake, None) == -1
     lib.zero_unfused_workspace_bytes.restype = C.c_size_t
     lib.zero_unfused_workspace_bytes.argtypes = [C.c_size_t, C.c_int]
-    assert lib.zero_unfused_workspace_bytes(1000, 2) >= 2 * 4000 + 3 * 64
+    assert lib.zero_unfused_workspace_bytes(1000, 2) >= 2 * 4000 + 3 * 128
     lib.zero_adamw_step_unfused.argtypes = [vp, vp, C.c_size_t, vp]
     assert lib.zero_adamw_step_unfused(None, fake, 1 << 20, None) == -1
 

@@ -122,7 +122,7 @@ def test_gpt2_small_p8_ten_steps_all_ranks(zs):
     # unsharded reference on the GPU: one rank holding the whole vector
     full = _step_for(zs, w, n=w.N, path="materialize")
     _init_state(full, w, 0)
-    accs = torch.zeros((w.P, 8), dtype=torch.int64, device="cuda")
+    accs = zs.new_norm_acc(w.P)
     reps = None
     # oracle: rank 0 in full, global norm from all ranks
     master = synth.fill(w.master_spec(), 0, w.S, False)
@@ -174,8 +174,7 @@ def _oracle_gates(w, calls):
     gates = []
     for call in calls:
         acc = oracle_norm_parallel(w, call, w.shard_start(), w.shard_start() + w.S)
-        skip = bool(w.check_overflow and (acc.nonfinite + acc.overflow) > 0)
-        coef = 1.0 if skip else O.clip_coef(O.acc_sumsq(acc), w.max_norm)
+        skip, coef = O.gate(acc, w.max_norm, w.check_overflow)
         gates.append((coef, skip))
     return gates
 

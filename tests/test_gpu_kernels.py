@@ -62,8 +62,9 @@ def test_shard_reduce_and_norm(zs, P, bf16):
         inject = [(P - 1, n - 1, np.inf)] if n > 5 else []
         if n > 100:
             inject += [(0, 3, np.nan), (P // 2, n // 2, -np.inf)]
-            if not bf16:
-                inject += [(0, 40, 2.0 ** 36)]    # finite, but its group overflows 2^64
+            # large finite values: group sums of squares past 2^64, and one
+            # near the top of binary32 (about 2^256): every group counts
+            inject += [(0, 40, 2.0 ** 36), (P // 2, 72, 3.0e38 / P), (P - 1, 75, -1.0e10)]
         reps = _replicas(P, n, bf16, seed=n, inject=inject)
         inv = O.inv_scale(P, 1.0)
         want_g = O.reduce(reps, inv)
@@ -86,11 +87,11 @@ def test_shard_reduce_and_norm(zs, P, bf16):
         ws = zs.new_reduce_workspace()
         g3 = torch.empty(n, dtype=torch.float32, device="cuda")
         acc3 = zs.new_norm_acc(1)
-        zs.zero_shard_reduce(dreps, inv, g_out=g3, acc=acc3, workspace=ws)
+        zs.zero_shard_reduce_ws(dreps, inv, ws, g_out=g3, acc=acc3)
         acc4 = zs.new_norm_acc(1)
-        zs.zero_shard_reduce(dreps, inv, acc=acc4, workspace=ws)
+        zs.zero_shard_reduce_ws(dreps, inv, ws, acc=acc4)
         g4 = torch.empty(n, dtype=torch.float32, device="cuda")
-        zs.zero_shard_reduce(dreps, inv, g_out=g4, workspace=ws)
+        zs.zero_shard_reduce_ws(dreps, inv, ws, g_out=g4)
         torch.cuda.synchronize()
         assert same_bits(from_dev(g3), want_g), n
         assert same_bits(from_dev(g4), want_g), n
@@ -128,8 +129,11 @@ def test_buckets_and_grid_shapes_do_not_change_the_norm(zs):
             acc = zs.new_norm_acc(1)
             for lo in range(0, n, bucket):
                 hi = min(n, lo + bucket)
-                zs.zero_shard_reduce([r[lo:hi] for r in reps], inv, acc=acc,
-                                     workspace=workspace)
+                views = [r[lo:hi] for r in reps]
+                if workspace is None:
+                    zs.zero_shard_reduce(views, inv, acc=acc)
+                else:
+                    zs.zero_shard_reduce_ws(views, inv, workspace, acc=acc)
             torch.cuda.synchronize()
             assert zs.read_norm_acc(acc) == zs.read_norm_acc(whole), (bucket, workspace)
     assert int(ws.abs().sum().item()) == 0
@@ -151,7 +155,7 @@ def test_one_shot_reduce_folds_many_slots(zs, P, bf16):
     g = torch.empty(n, dtype=torch.float32, device="cuda")
     accs = zs.new_norm_acc(3)
     for k in range(3):
-        zs.zero_shard_reduce(dreps, inv, g_out=g, acc=accs[k], workspace=ws)
+        zs.zero_shard_reduce_ws(dreps, inv, ws, g_out=g, acc=accs[k])
     torch.cuda.synchronize()
     assert same_bits(from_dev(g), want_g), mismatch_report("g", from_dev(g), want_g)
     assert zs.read_norm_acc(accs) == [want_acc] * 3
@@ -236,7 +240,7 @@ def test_mx_reduce_and_norm(zs, P):
         ws = zs.new_reduce_workspace()
         g3 = torch.empty(n, dtype=torch.float32, device="cuda")
         acc3 = zs.new_norm_acc(1)
-        zs.zero_shard_reduce_mx(codes, scales, inv, g_out=g3, acc=acc3, workspace=ws)
+        zs.zero_shard_reduce_mx_ws(codes, scales, inv, ws, g_out=g3, acc=acc3)
         torch.cuda.synchronize()
         got = from_dev(g)
         assert _same_or_both_nan(got, want_g), mismatch_report(f"g n={n}", got, want_g)
@@ -297,51 +301,58 @@ def test_shard_step_with_mxfp8_gradients(zs, oneshot_min):
 
 # ------------------------------------------------------------------ gate --
 
-def _acc_words(X, nonfinite, overflow, rng):
-    """Device layout of an accumulator holding X, with pending carries."""
-    d = [(X >> (32 * k)) & 0xFFFFFFFF for k in range(7)]
-    d[6] += (X >> 224) << 32 if X >> 224 else 0
-    for k in range(6, 0, -1):          # push some value down as pending carries
+ACC_DIGITS = 13
+
+
+def _acc_words(X, nonfinite, rng):
+    """Device layout of an accumulator holding X (13 digits with pending
+    carries, the non-finite count, two reserved zero words)."""
+    d = [(X >> (32 * k)) & 0xFFFFFFFF for k in range(ACC_DIGITS)]
+    d[-1] += (X >> (32 * ACC_DIGITS)) << 32
+    for k in range(ACC_DIGITS - 1, 0, -1):   # push some value down as pending carries
         c = int(rng.integers(0, min(d[k], 1 << 31) + 1)) if d[k] else 0
         d[k] -= c
         d[k - 1] += c << 32
+    assert all(0 <= v < (1 << 64) for v in d)
     words = [v - (1 << 64) if v >= (1 << 63) else v for v in d]
-    tail = (overflow << 32) | nonfinite
-    words.append(tail - (1 << 64) if tail >= (1 << 63) else tail)
-    return words
+    return words + [nonfinite, 0, 0]
 
 
 def test_gate_matches_oracle(zs):
+    """The device gate (the AdamW prologue's) against the oracle's over
+    accumulator values up to the 13 digits' range (including RNE ties and
+    pending carries), several thresholds, and the skip / clip-to-zero rules."""
     import torch
     rng = np.random.default_rng(21)
+    top = 1 << (32 * ACC_DIGITS + 20)
     Xs = [0, 1, 3, (1 << 53) - 1, 1 << 53, (1 << 53) + 1, (1 << 54) + 2, (1 << 54) + 6,
-          25 << 128, (1 << 224) - 1]
-    for bits in range(1, 224, 2):
+          25 << 128, (1 << 224) - 1, 1 << 224, (1 << 389) - 1, 281474943156225 << 341]
+    for bits in range(1, 32 * ACC_DIGITS + 18, 3):
         Xs.append(int(rng.integers(1, 1 << 62)) << max(0, bits - 62))
     for m in ((1 << 52) + 1, (1 << 53) - 1):
-        for sh in (1, 60, 150):
+        for sh in (1, 60, 150, 300):
             Xs += [(2 * m + 1) << sh, ((2 * m + 1) << sh) + 1, ((2 * m + 1) << sh) - 1]
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
     skip = torch.empty(1, dtype=torch.int32, device="cuda")
     rows, expect = [], []
     for X in Xs:
-        X &= (1 << 224) - 1
-        for max_norm in (1.0, 0.37, 1e6, 0.0):
-            for nonfinite, overflow, check in ((0, 0, 1), (2, 0, 1), (0, 1, 1), (3, 0, 0)):
+        X %= top
+        for max_norm in (1.0, 0.37, 1e6, 1e200, 0.0):
+            for nonfinite, check in ((0, 1), (2, 1), (3, 0), (0, 0)):
                 parts = [X // 3, X // 3, X - 2 * (X // 3)]
                 words = []
                 oacc = O.acc_zero()
                 for j, part in enumerate(parts):
                     nf = nonfinite if j == 0 else 0
-                    words.append(_acc_words(part, nf, overflow if j == 2 else 0, rng))
+                    words.append(_acc_words(part, nf, rng))
                     a = O.acc_zero()
-                    for k in range(8):
+                    for k in range(O.ACC_WORDS):
                         a.w[k] = (part >> (32 * k)) & 0xFFFFFFFF
+                    a.nonfinite = nf
                     O.acc_add(oacc, a)
-                want_skip = int(check and (nonfinite + overflow) > 0)
-                want_coef = 1.0 if want_skip else O.clip_coef(O.acc_sumsq(oacc), max_norm)
+                want_skip, want_coef = O.gate(oacc, max_norm, check)
                 rows.append((words, max_norm, check))
-                expect.append((want_coef, want_skip, X))
+                expect.append((want_coef, int(want_skip), X))
     got = []
     for words, max_norm, check in rows:
         accs = torch.tensor(words, dtype=torch.int64, device="cuda")
@@ -387,7 +398,8 @@ def test_adamw_multi_step(zs, source, gated):
                 g = O.reduce(reps, inv)
                 coef = 1.0
                 if gated:
-                    coef = O.clip_coef(O.acc_sumsq(O.norm_accumulate(g)), max_norm)
+                    skip, coef = O.gate(O.norm_accumulate(g), max_norm, True)
+                    assert not skip
                 O.adamw(g, coef, O.make_scalars(lr, b1, b2, eps, wd, t), master, m, v, param)
                 dreps = [to_dev(r) for r in reps]
                 kw = dict(step=t, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd,
@@ -490,46 +502,104 @@ def test_adamw_skip_leaves_state_untouched(zs):
 
 
 @pytest.mark.timeout(600)
-def test_adamw_and_pack_past_2_32_elements(zs):
-    """64-bit indexing: one AdamW step and the MXFP8 pack on n > 2^32
-    elements (about 78 GB of state), sampled around the 2^31 and 2^32
-    element boundaries and the ragged end."""
+def test_gated_step_past_2_32_elements(zs):
+    """64-bit indexing and one norm call over more than 2^32 elements: a
+    gated step (clip 1.0 and the overflow check) of one bf16 replica on
+    n > 2^32 elements (about 73 GB of state), with the MXFP8 pack fused.  One
+    gradient of 2^34 (a group norm of about 1.7e10, past the old 2^32 group
+    limit) dominates the norm, so the clip coefficient depends on it.  The
+    oracle computes the global norm over all n elements on the host, then
+    follows sampled blocks around the 2^31 and 2^32 element boundaries, the
+    large gradient and the ragged end."""
     import torch
+    from synth.configs import Workload
+    from gpu_util import oracle_norm_parallel
     n = (1 << 32) + 4096 + 32 * 3
-    gspec = synth.make_spec(seed=1, cfg=55, stream=1, sigma=1e-3)
-    mspec = synth.make_spec(seed=1, cfg=55, stream=0, sigma=0.02)
-    g = torch.empty(n, dtype=torch.float32, device="cuda")
-    master = torch.empty(n, dtype=torch.float32, device="cuda")
-    synth.fill_device(gspec, 0, g)
-    synth.fill_device(mspec, 0, master)
-    m = torch.zeros(n, dtype=torch.float32, device="cuda")
-    v = torch.zeros(n, dtype=torch.float32, device="cuda")
-    param = torch.empty(n, dtype=torch.int16, device="cuda")
-    elem = torch.empty(n, dtype=torch.uint8, device="cuda")
-    scale = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
-    zs.zero_adamw_step(master, m, v, grad_f32=g, step=1, lr=1e-3, weight_decay=0.01,
-                       param_bf16=param, mx_elem_out=elem, mx_scale_out=scale)
-    acc = zs.new_norm_acc(1)
-    with pytest.raises(zs.ZeroStepError):
-        zs.zero_grad_norm(g, 1.0, acc)                       # n >= 2^32: ESIZE
+    big_at, big = (1 << 32) + 37, 0x5080                 # bf16 bits of 2^34
+    w = Workload("past-2^32", "one bf16 replica past 2^32 elements", N=n, P=1, S=n,
+                 grad_bf16=True, grad_sigma=1e-3, steps=1, max_norm=1.0, check_overflow=True,
+                 pack=True, cfg_id=55, seed=1)
+    st = zs.ShardStep(n, 1, torch.bfloat16, lr=w.lr, weight_decay=w.wd, max_norm=w.max_norm,
+                      check_overflow=True, pack=True)
+    assert st.path == "recompute"
+    rep = torch.empty(n, dtype=torch.int16, device="cuda")
+    synth.fill_device(w.grad_spec(1, 0), 0, rep)
+    rep[big_at] = big
+    synth.fill_device(w.master_spec(), 0, st.master)
+    synth.fill_device(w.master_spec(), 0, st.param)
+    st.step([rep])
     torch.cuda.synchronize()
-    blocks = np.array([0, (1 << 26) - 1, 1 << 26, (1 << 27) - 1, 1 << 27, n // 32 - 1],
-                      dtype=np.int64)
+    assert st.applied_steps() == 1
+    print("gated step past 2^32: GPU done, oracle norm over", n, "elements", flush=True)
+    # the oracle's global norm state: the group holding the large gradient
+    # on its own, the rest split at that group's 32-aligned bounds
+    g0 = big_at // 32 * 32
+    acc = oracle_norm_parallel(w, 1, 0, g0)
+    O.acc_add(acc, oracle_norm_parallel(w, 1, g0 + 32, n))
+    grp = synth.fill(w.grad_spec(1, 0), g0, 32, True)
+    grp[big_at - g0] = big
+    O.acc_add(acc, O.norm_accumulate(O.reduce([grp], 1.0)))
+    skip, coef = O.gate(acc, w.max_norm, True)
+    assert not skip and 0 < coef < 1e-9
+    assert zs.read_norm_acc(st.acc)[0] == (acc.X, int(acc.nonfinite))
+    blocks = np.array([0, (1 << 26) - 1, 1 << 26, (1 << 27) - 1, 1 << 27, big_at // 32,
+                       n // 32 - 1], dtype=np.int64)
     idx = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
     di = torch.from_numpy(idx).cuda()
-    hg = synth.gather(gspec, idx.astype(np.uint64), False)
-    hmaster = synth.gather(mspec, idx.astype(np.uint64), False)
+    hg = synth.gather(w.grad_spec(1, 0), idx.astype(np.uint64), True)
+    hg[idx == big_at] = big
+    hmaster = synth.gather(w.master_spec(), idx.astype(np.uint64), False)
     hm, hv = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
     hparam = np.zeros(idx.size, np.uint16)
-    O.adamw(hg, 1.0, O.make_scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, 1), hmaster, hm, hv, hparam)
+    O.adamw(O.reduce([hg], 1.0), coef, O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, 1),
+            hmaster, hm, hv, hparam)
     we, ws = O.mxfp8_pack(hparam)
-    assert same_bits(from_dev(master[di]), hmaster)
-    assert same_bits(from_dev(m[di]), hm) and same_bits(from_dev(v[di]), hv)
-    assert same_bits(from_dev(param[di], True), hparam)
-    assert np.array_equal(from_dev(elem[di]), we)
-    assert np.array_equal(from_dev(scale[torch.from_numpy(blocks).cuda()]), ws)
-    del g, master, m, v, param, elem, scale
+    assert same_bits(from_dev(st.master[di]), hmaster)
+    assert same_bits(from_dev(st.m[di]), hm) and same_bits(from_dev(st.v[di]), hv)
+    assert same_bits(from_dev(st.param[di], True), hparam)
+    assert np.array_equal(from_dev(st.mx_elem[di]), we)
+    assert np.array_equal(from_dev(st.mx_scale[torch.from_numpy(blocks).cuda()]), ws)
+    del st, rep
     torch.cuda.empty_cache()
+
+
+def test_clip_only_counts_large_groups_and_zeroes_on_nonfinite(zs):
+    """Clipping without the overflow check, four calls: ordinary gradients;
+    one averaged gradient of about 1.25e10 (its group's sum of squares past 2^64 counts
+    in full and sets the coefficient); one infinite gradient (the norm is
+    infinite, the coefficient 0: every finite element steps with a zero
+    gradient and the infinite one's state becomes NaN); ordinary again.
+    Against the oracle bit for bit, except that a NaN result is compared as
+    NaN: IEEE 754 leaves the sign and payload of a NaN made by inf * 0
+    unspecified, and the two processors make different ones."""
+    import torch
+    n, P = 32 * 4099 + 5, 8
+    lr, b1, b2, eps, wd, max_norm = 1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0
+    master = synth.fill(synth.make_spec(seed=8, cfg=57, stream=0, sigma=0.02), 0, n, False)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    param = O.f32_to_bf16(master)
+    st = zs.ShardStep(n, P, torch.bfloat16, lr=lr, beta1=b1, beta2=b2, eps=eps,
+                      weight_decay=wd, max_norm=max_norm, check_overflow=False)
+    st.master.copy_(to_dev(master))
+    st.param.copy_(to_dev(param))
+    coefs = []
+    for call in range(1, 5):
+        inject = {2: [(3, 1000, 1.0e11)], 3: [(5, 77, -np.inf)]}.get(call, [])
+        reps = _replicas(P, n, True, seed=41 * call, inject=inject)
+        _, acc = O.step(reps, O.inv_scale(P, 1.0), max_norm, False, lr, b1, b2, eps, wd, call,
+                        master, m, v, param)
+        coefs.append(O.gate(acc, max_norm, False)[1])
+        st.step([to_dev(r) for r in reps])
+    assert coefs[2] == 0.0 and 0 < coefs[1] < 1e-9
+    torch.cuda.synchronize()
+    for name, want in (("master", master), ("m", m), ("v", v), ("param", param)):
+        got = from_dev(getattr(st, name), name == "param")
+        wf = O.bf16_to_f32(want) if name == "param" else want
+        gf = O.bf16_to_f32(got) if name == "param" else got
+        nan = np.isnan(wf)
+        assert nan.sum() == 1 and nan[77]
+        assert np.array_equal(np.isnan(gf), nan), name
+        assert same_bits(got[~nan], want[~nan]), mismatch_report(name, got[~nan], want[~nan])
 
 
 @pytest.mark.parametrize("P,bf16", [(1, True), (3, True), (4, False), (8, True)])
@@ -684,7 +754,7 @@ def test_zero_length_calls_touch_nothing(zs):
     zs.zero_mxfp8_pack(reps[0], elem, scale, n=0)
     torch.cuda.synchronize()
     assert torch.all(g == 7.0).item()
-    assert zs.read_norm_acc(acc)[0] == (0, 0, 0)
+    assert zs.read_norm_acc(acc)[0] == (0, 0)
     assert torch.all(elem == 0xAB).item() and torch.all(scale == 0xCD).item()
 
     bad = zs.new_norm_acc(1)

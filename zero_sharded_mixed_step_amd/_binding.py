@@ -13,10 +13,11 @@ import torch
 from . import build as _build
 
 ZERO_F32, ZERO_BF16, ZERO_MXFP8 = 0, 1, 2
-ABI_VERSION = 4        # the zero_step.h this binding's structs follow
+ABI_VERSION = 5        # the zero_step.h this binding's structs follow
 ZERO_MAX_REPLICAS = 64
-ACC_WORDS = 8          # one zero_norm_acc = 64 bytes = 8 int64 words
-REDUCE_WORKSPACE_BYTES = 64 * 512   # ZERO_REDUCE_WORKSPACE_BYTES
+ACC_WORDS = 16         # one zero_norm_acc = 128 bytes = 16 int64 words
+ACC_DIGITS = 13        # digit[13]; then nonfinite, reserved[2]
+REDUCE_WORKSPACE_BYTES = 128 * 512   # ZERO_REDUCE_WORKSPACE_BYTES
 
 _lib = None
 
@@ -54,17 +55,19 @@ def lib():
         L.zero_inv_scale.argtypes = [i, C.c_double]
         L.zero_inv_scale.restype = C.c_float
         L.zero_norm_acc_clear.argtypes = [vp, i, vp]
-        L.zero_shard_reduce.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp, sz, vp]
+        L.zero_shard_reduce.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp]
+        L.zero_shard_reduce_ws.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp, sz, vp]
         L.zero_grad_norm.argtypes = [vp, i, sz, C.c_float, vp, vp]
         L.zero_adamw_step.argtypes = [C.POINTER(_AdamArgs), vp]
         L.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
         L.zero_mxfp8_pack.argtypes = [vp, sz, vp, vp, vp]
-        L.zero_shard_reduce_mx.argtypes = [vp, vp, i, sz, C.c_float, vp, vp, vp, sz, vp]
-        L.zero_shard_reduce_mx.restype = i
+        L.zero_shard_reduce_mx.argtypes = [vp, vp, i, sz, C.c_float, vp, vp, vp]
+        L.zero_shard_reduce_mx_ws.argtypes = [vp, vp, i, sz, C.c_float, vp, vp, vp, sz, vp]
         L.zero_unfused_workspace_bytes.argtypes = [sz, i]
         L.zero_unfused_workspace_bytes.restype = sz
         L.zero_adamw_step_unfused.argtypes = [C.POINTER(_AdamArgs), vp, sz, vp]
-        for f in (L.zero_norm_acc_clear, L.zero_shard_reduce, L.zero_grad_norm,
+        for f in (L.zero_norm_acc_clear, L.zero_shard_reduce, L.zero_shard_reduce_ws,
+                  L.zero_shard_reduce_mx, L.zero_shard_reduce_mx_ws, L.zero_grad_norm,
                   L.zero_adamw_step, L.zero_step_gate, L.zero_mxfp8_pack,
                   L.zero_adamw_step_unfused):
             f.restype = i
@@ -132,7 +135,7 @@ def _acc_ptr(acc):
     if acc is None:
         return None, 0
     if acc.dtype != torch.int64 or acc.numel() % ACC_WORDS:
-        raise TypeError("norm accumulators are int64 tensors of shape (k, 8)")
+        raise TypeError(f"norm accumulators are int64 tensors of shape (k, {ACC_WORDS})")
     return _dev_ptr(acc, "acc"), acc.numel() // ACC_WORDS
 
 
@@ -153,14 +156,15 @@ def zero_inv_scale(P: int, loss_scale: float = 1.0) -> float:
 def new_reduce_workspace(device="cuda") -> torch.Tensor:
     """A zeroed reduce workspace (ZERO_REDUCE_WORKSPACE_BYTES, as int64 words
     so that zero_norm_acc_clear can zero it)."""
-    ws = torch.empty((REDUCE_WORKSPACE_BYTES // 64, ACC_WORDS), dtype=torch.int64, device=device)
+    ws = torch.empty((REDUCE_WORKSPACE_BYTES // (8 * ACC_WORDS), ACC_WORDS), dtype=torch.int64,
+                     device=device)
     zero_norm_acc_clear(ws)
     return ws
 
 
 def _ws_ptr(workspace):
     if workspace is None:
-        return None, 0
+        raise ValueError("the _ws entry points need a workspace (new_reduce_workspace())")
     nbytes = workspace.numel() * workspace.element_size()
     if nbytes < REDUCE_WORKSPACE_BYTES:
         raise ValueError(f"reduce workspace holds {nbytes} bytes, needs {REDUCE_WORKSPACE_BYTES}")
@@ -168,22 +172,21 @@ def _ws_ptr(workspace):
 
 
 def new_norm_acc(k: int = 1, device="cuda") -> torch.Tensor:
-    """k zeroed accumulators (64 bytes each) as an int64 (k, 8) tensor."""
+    """k zeroed accumulators (128 bytes each) as an int64 (k, 16) tensor."""
     acc = torch.empty((k, ACC_WORDS), dtype=torch.int64, device=device)
     zero_norm_acc_clear(acc)
     return acc
 
 
 def read_norm_acc(acc: torch.Tensor):
-    """Host view of accumulators: list of (X, nonfinite, overflow) with X the
-    integer whose value times 2^-128 is the sum of squares."""
+    """Host view of accumulators: list of (X, nonfinite) with X the integer
+    whose value times 2^-128 is the sum of squares."""
     words = acc.detach().reshape(-1, ACC_WORDS).cpu().tolist()
     out = []
     for w in words:
-        digits = [d & 0xFFFFFFFFFFFFFFFF for d in w[:7]]
-        tail = w[7] & 0xFFFFFFFFFFFFFFFF
+        digits = [d & 0xFFFFFFFFFFFFFFFF for d in w[:ACC_DIGITS]]
         X = sum(d << (32 * k) for k, d in enumerate(digits))
-        out.append((X, tail & 0xFFFFFFFF, tail >> 32))
+        out.append((X, w[ACC_DIGITS] & 0xFFFFFFFFFFFFFFFF))
     return out
 
 
@@ -194,8 +197,7 @@ def zero_norm_acc_clear(accs: torch.Tensor, stream=None) -> None:
     _check(lib().zero_norm_acc_clear(p, k, _stream(stream)), "zero_norm_acc_clear")
 
 
-def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
-                      workspace=None, stream=None) -> None:
+def _reduce_args(replicas, n, g_out, acc, name):
     reps = list(replicas)
     if not reps:
         raise ValueError("at least one replica")
@@ -207,17 +209,31 @@ def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
     _need(g_out, n, "g_out", F32)
     ap, k = _acc_ptr(acc)
     if k > 1:
-        raise ValueError("zero_shard_reduce adds to one accumulator")
-    wp, wb = _ws_ptr(workspace)
+        raise ValueError(f"{name} adds to one accumulator")
+    return reps, n, ap
+
+
+def zero_shard_reduce(replicas, inv_scale: float, g_out=None, acc=None, n=None,
+                      stream=None) -> None:
+    reps, n, ap = _reduce_args(replicas, n, g_out, acc, "zero_shard_reduce")
     _check(lib().zero_shard_reduce(_ptr_array(reps, "replica"), len(reps), _dtype_code(reps[0]),
-                                   n, float(inv_scale), _dev_ptr(g_out, "g_out"), ap, wp, wb,
+                                   n, float(inv_scale), _dev_ptr(g_out, "g_out"), ap,
                                    _stream(stream)), "zero_shard_reduce")
 
 
-def zero_shard_reduce_mx(codes, scales, inv_scale: float, g_out=None, acc=None, n=None,
-                         workspace=None, stream=None) -> None:
-    """Shard reduce of MXFP8-stored replicas: codes[k] uint8[n] and scales[k]
-    uint8[n/32] per rank (n % 32 == 0)."""
+def zero_shard_reduce_ws(replicas, inv_scale: float, workspace, g_out=None, acc=None, n=None,
+                         stream=None) -> None:
+    """zero_shard_reduce with the one-shot form's workspace
+    (new_reduce_workspace())."""
+    reps, n, ap = _reduce_args(replicas, n, g_out, acc, "zero_shard_reduce_ws")
+    wp, wb = _ws_ptr(workspace)
+    _check(lib().zero_shard_reduce_ws(_ptr_array(reps, "replica"), len(reps),
+                                      _dtype_code(reps[0]), n, float(inv_scale),
+                                      _dev_ptr(g_out, "g_out"), ap, wp, wb, _stream(stream)),
+           "zero_shard_reduce_ws")
+
+
+def _mx_args(codes, scales, n, g_out, acc, name):
     codes, scales = list(codes), list(scales)
     if not codes or len(codes) != len(scales):
         raise ValueError("one code array and one scale array per replica")
@@ -228,11 +244,28 @@ def zero_shard_reduce_mx(codes, scales, inv_scale: float, g_out=None, acc=None, 
     _need(g_out, n, "g_out", F32)
     ap, k = _acc_ptr(acc)
     if k > 1:
-        raise ValueError("zero_shard_reduce_mx adds to one accumulator")
-    wp, wb = _ws_ptr(workspace)
+        raise ValueError(f"{name} adds to one accumulator")
+    return codes, scales, n, ap
+
+
+def zero_shard_reduce_mx(codes, scales, inv_scale: float, g_out=None, acc=None, n=None,
+                         stream=None) -> None:
+    """Shard reduce of MXFP8-stored replicas: codes[k] uint8[n] and scales[k]
+    uint8[n/32] per rank (n % 32 == 0)."""
+    codes, scales, n, ap = _mx_args(codes, scales, n, g_out, acc, "zero_shard_reduce_mx")
     _check(lib().zero_shard_reduce_mx(_ptr_array(codes, "codes"), _ptr_array(scales, "scales"),
                                       len(codes), n, float(inv_scale), _dev_ptr(g_out, "g_out"),
-                                      ap, wp, wb, _stream(stream)), "zero_shard_reduce_mx")
+                                      ap, _stream(stream)), "zero_shard_reduce_mx")
+
+
+def zero_shard_reduce_mx_ws(codes, scales, inv_scale: float, workspace, g_out=None, acc=None,
+                            n=None, stream=None) -> None:
+    codes, scales, n, ap = _mx_args(codes, scales, n, g_out, acc, "zero_shard_reduce_mx_ws")
+    wp, wb = _ws_ptr(workspace)
+    _check(lib().zero_shard_reduce_mx_ws(_ptr_array(codes, "codes"),
+                                         _ptr_array(scales, "scales"), len(codes), n,
+                                         float(inv_scale), _dev_ptr(g_out, "g_out"), ap, wp,
+                                         wb, _stream(stream)), "zero_shard_reduce_mx_ws")
 
 
 def zero_grad_norm(grad, inv_scale: float, acc, n=None, stream=None) -> None:

@@ -17,6 +17,10 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Elements one accumulator can take: 2^32 norm groups of 32, so that no
+// digit, which receives one piece below 2^32 per group, can wrap.
+constexpr size_t kMaxNormElems = size_t(1) << 37;
+
 int status_of(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_EHIP; }
 
 int check_replicas(const void* const* replicas, int P, int dtype) {
@@ -47,9 +51,10 @@ const char* zero_strerror(int status) {
     case ZERO_OK: return "ok";
     case ZERO_EINVAL: return "invalid argument (null pointer, replica count, dtype, step or "
                              "gradient source)";
-    case ZERO_EALIGN: return "device pointer not 16-byte aligned";
-    case ZERO_ESIZE: return "size not supported (MXFP8 needs n % 32 == 0; a norm call needs "
-                            "n < 2^32; a reduce workspace needs ZERO_REDUCE_WORKSPACE_BYTES)";
+    case ZERO_EALIGN: return "pointer misaligned (device arrays and accumulators need 16 "
+                             "bytes, int32/float outputs 4, the step counter 8)";
+    case ZERO_ESIZE: return "size not supported (MXFP8 needs n % 32 == 0; a norm call takes "
+                            "n <= 2^37; a reduce workspace needs ZERO_REDUCE_WORKSPACE_BYTES)";
     case ZERO_EHIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -72,9 +77,12 @@ int zero_norm_acc_clear(zero_norm_acc* accs, int n_accs, void* stream) {
   }
 }
 
-int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, float inv_scale,
-                      float* g_out, zero_norm_acc* acc, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+namespace {
+
+// The reduce with an optional workspace (the one-shot form when given).
+int reduce_call(const void* const* replicas, int P, int dtype, size_t n, float inv_scale,
+                float* g_out, zero_norm_acc* acc, void* workspace, size_t workspace_bytes,
+                void* stream) {
   try {
     const int rc = check_replicas(replicas, P, dtype);
     if (rc != ZERO_OK) return rc;
@@ -82,7 +90,7 @@ int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, f
     if ((g_out && !aligned16(g_out)) || (acc && !aligned16(acc))) return ZERO_EALIGN;
     const int wc = check_workspace(workspace, workspace_bytes);
     if (wc != ZERO_OK) return wc;
-    if (acc != nullptr && n >= (size_t(1) << 32)) return ZERO_ESIZE;
+    if (acc != nullptr && n > kMaxNormElems) return ZERO_ESIZE;
     if (n == 0) return ZERO_OK;
     return status_of(zs::launch_reduce(replicas, P, dtype, n, inv_scale, g_out, acc,
                                        as_stream(stream), nullptr, workspace));
@@ -91,9 +99,9 @@ int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, f
   }
 }
 
-int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scales, int P,
-                         size_t n, float inv_scale, float* g_out, zero_norm_acc* acc,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+int reduce_mx_call(const uint8_t* const* codes, const uint8_t* const* scales, int P, size_t n,
+                   float inv_scale, float* g_out, zero_norm_acc* acc, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   try {
     if (codes == nullptr || scales == nullptr || P < 1 || P > ZERO_MAX_REPLICAS)
       return ZERO_EINVAL;
@@ -105,7 +113,7 @@ int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scal
     if ((g_out && !aligned16(g_out)) || (acc && !aligned16(acc))) return ZERO_EALIGN;
     const int wc = check_workspace(workspace, workspace_bytes);
     if (wc != ZERO_OK) return wc;
-    if (n % 32 != 0 || (acc != nullptr && n >= (size_t(1) << 32))) return ZERO_ESIZE;
+    if (n % 32 != 0 || (acc != nullptr && n > kMaxNormElems)) return ZERO_ESIZE;
     if (n == 0) return ZERO_OK;
     const void* c[ZERO_MAX_REPLICAS];
     const void* sc[ZERO_MAX_REPLICAS];
@@ -120,6 +128,35 @@ int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scal
   }
 }
 
+}  // namespace
+
+int zero_shard_reduce(const void* const* replicas, int P, int dtype, size_t n, float inv_scale,
+                      float* g_out, zero_norm_acc* acc, void* stream) {
+  return reduce_call(replicas, P, dtype, n, inv_scale, g_out, acc, nullptr, 0, stream);
+}
+
+int zero_shard_reduce_ws(const void* const* replicas, int P, int dtype, size_t n,
+                         float inv_scale, float* g_out, zero_norm_acc* acc, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return ZERO_EINVAL;
+  return reduce_call(replicas, P, dtype, n, inv_scale, g_out, acc, workspace, workspace_bytes,
+                     stream);
+}
+
+int zero_shard_reduce_mx(const uint8_t* const* codes, const uint8_t* const* scales, int P,
+                         size_t n, float inv_scale, float* g_out, zero_norm_acc* acc,
+                         void* stream) {
+  return reduce_mx_call(codes, scales, P, n, inv_scale, g_out, acc, nullptr, 0, stream);
+}
+
+int zero_shard_reduce_mx_ws(const uint8_t* const* codes, const uint8_t* const* scales, int P,
+                            size_t n, float inv_scale, float* g_out, zero_norm_acc* acc,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return ZERO_EINVAL;
+  return reduce_mx_call(codes, scales, P, n, inv_scale, g_out, acc, workspace,
+                        workspace_bytes, stream);
+}
+
 int zero_grad_norm(const void* grad, int dtype, size_t n, float inv_scale, zero_norm_acc* acc,
                    void* stream) {
   try {
@@ -128,7 +165,7 @@ int zero_grad_norm(const void* grad, int dtype, size_t n, float inv_scale, zero_
     const int rc = check_replicas(reps, 1, dtype);
     if (rc != ZERO_OK) return rc;
     if (!aligned16(acc)) return ZERO_EALIGN;
-    if (n >= (size_t(1) << 32)) return ZERO_ESIZE;
+    if (n > kMaxNormElems) return ZERO_ESIZE;
     if (n == 0) return ZERO_OK;
     return status_of(
         zs::launch_reduce(reps, 1, dtype, n, inv_scale, nullptr, acc, as_stream(stream)));
@@ -214,7 +251,7 @@ int zero_adamw_step_unfused(const zero_adamw_args* a, void* workspace, size_t wo
     if (rc != ZERO_OK) return rc;
     if (a->mx_elem_out != nullptr && a->param_bf16 == nullptr) return ZERO_EINVAL;
     if (a->step_dev != nullptr) return ZERO_EINVAL;  // the chain takes the host counter
-    if (a->n >= (size_t(1) << 32)) return ZERO_ESIZE;  // the chain's own norm accumulator
+    if (a->n > kMaxNormElems) return ZERO_ESIZE;  // the chain's own norm accumulator
     if (workspace == nullptr) return ZERO_EINVAL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ZERO_EALIGN;
     if (workspace_bytes < zs::unfused_workspace_bytes(a->n, a->n_accs)) return ZERO_ESIZE;

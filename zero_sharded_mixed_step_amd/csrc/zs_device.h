@@ -18,6 +18,10 @@ namespace zs {
 
 constexpr int kThreads = 256;  // four wave64 wavefronts per workgroup
 constexpr int kVec = 8;        // elements per chunk
+constexpr int kDigits = 13;    // 32-bit digit positions of the norm's fixed point
+static_assert(sizeof(zero_norm_acc) == 128 &&
+                  sizeof(((zero_norm_acc*)nullptr)->digit) == kDigits * 8,
+              "accumulator layout");
 
 struct Replicas {
   const void* p[ZERO_MAX_REPLICAS];  // element data (MXFP8: the E4M3 codes)
@@ -278,15 +282,18 @@ __device__ __forceinline__ double quad_group_sum(double a) {
 }
 
 // floor(S * 2^128) split into three 32-bit pieces p0, p1, p2 at digits
-// base, base+1, base+2 (base + 2 <= 6).  S >= 0; a zero or subnormal S
-// (below 2^-1022, so below one unit) or one >= 2^64 gives three zero pieces.
+// base, base+1, base+2.  0 <= S < 2^262 (a group of finite binary32 values
+// gives S < 2^261), so the exponent field is at most 1284, sh below at most
+// 337 and base + 2 <= 12 = kDigits - 1.  A zero or subnormal S (below
+// 2^-1022, so below one unit) gives three zero pieces; so would anything
+// outside that range, which keeps every digit index in bounds.
 __device__ __forceinline__ void fixed_point_split(double S, int& base, uint32_t& p0,
                                                   uint32_t& p1, uint32_t& p2) {
   const uint64_t bits = __double_as_longlong(S);
   const int ex = static_cast<int>((bits >> 52) & 0x7FF);
   base = 0;
   p0 = p1 = p2 = 0u;
-  if (ex == 0 || ex >= 1087) return;
+  if (ex == 0 || ex > 1284) return;
   const uint64_t mant = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
   const int sh = ex - 947;  // S * 2^128 = mant * 2^sh
   if (sh < 0) {
@@ -413,45 +420,48 @@ struct Gate {
   int32_t skip;
 };
 
-// Sum of the accumulators as a normalised 256-bit integer (8 x 32 bits).
-__device__ inline void acc_total(const zero_norm_acc* accs, int n_accs, uint32_t w[8],
-                                 uint64_t& nonfinite, uint64_t& overflow) {
+// Words of the accumulators' normalised sum: 13 digits of 32 bits with up
+// to 32 pending carry bits each, summed over up to 2^31 accumulators, stay
+// below 2^(32*16).
+constexpr int kSumWords = 16;
+
+// Sum of the accumulators as a normalised 512-bit integer (16 x 32 bits).
+__device__ inline void acc_total(const zero_norm_acc* accs, int n_accs, uint32_t w[kSumWords],
+                                 uint64_t& nonfinite) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) w[k] = 0u;
+  for (int k = 0; k < kSumWords; ++k) w[k] = 0u;
   nonfinite = 0;
-  overflow = 0;
   for (int a = 0; a < n_accs; ++a) {
-    uint32_t t[8];
+    uint32_t t[kDigits + 1];
     uint64_t carry = 0;
 #pragma unroll
-    for (int k = 0; k < 7; ++k) {
+    for (int k = 0; k < kDigits; ++k) {
       const uint64_t x = accs[a].digit[k];
       const uint64_t s = (x & 0xFFFFFFFFull) + carry;
       t[k] = static_cast<uint32_t>(s);
       carry = (x >> 32) + (s >> 32);
     }
-    t[7] = static_cast<uint32_t>(carry);
+    t[kDigits] = static_cast<uint32_t>(carry);
     uint64_t c2 = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint64_t s = static_cast<uint64_t>(w[k]) + t[k] + c2;
+    for (int k = 0; k < kSumWords; ++k) {
+      const uint64_t s = static_cast<uint64_t>(w[k]) + (k <= kDigits ? t[k] : 0u) + c2;
       w[k] = static_cast<uint32_t>(s);
       c2 = s >> 32;
     }
     nonfinite += accs[a].nonfinite;
-    overflow += accs[a].overflow;
   }
 }
 
-// RNE_binary64(X * 2^-128) for X held in w[0..7].
-__device__ inline double fixed_to_double(const uint32_t w[8]) {
+// RNE_binary64(X * 2^-128) for X held in w[0..kSumWords).
+__device__ inline double fixed_to_double(const uint32_t w[kSumWords]) {
   int top_word = -1;
 #pragma unroll
-  for (int k = 7; k >= 0; --k)
+  for (int k = kSumWords - 1; k >= 0; --k)
     if (top_word < 0 && w[k] != 0u) top_word = k;
   if (top_word < 0) return 0.0;
   const int top = 32 * top_word + (31 - __clz(static_cast<int>(w[top_word])));
-  // bit(pos) of the 256-bit number
+  // bit(pos) of the 512-bit number
   auto bit = [&](int pos) -> uint32_t {
     return pos < 0 ? 0u : ((w[pos >> 5] >> (pos & 31)) & 1u);
   };
@@ -466,14 +476,14 @@ __device__ inline double fixed_to_double(const uint32_t w[8]) {
     // bits [s, s+52] via a funnel over three words
     const int i = s >> 5, off = s & 31;
     const uint64_t lo = (static_cast<uint64_t>(w[i + 1]) << 32) | w[i];
-    const uint64_t hi = (i + 2 < 8) ? w[i + 2] : 0u;
+    const uint64_t hi = (i + 2 < kSumWords) ? w[i + 2] : 0u;
     mant = off ? ((lo >> off) | (hi << (64 - off))) : lo;
     mant &= (1ull << 53) - 1ull;
     const uint32_t round_bit = bit(s - 1);
     uint32_t sticky = 0;
     // everything below s-1
     const int below = s - 1;  // number of bits under the rounding bit
-    for (int k = 0; k < 8 && 32 * k < below; ++k) {
+    for (int k = 0; k < kSumWords && 32 * k < below; ++k) {
       const int hi_bits = below - 32 * k;  // bits of word k that are below
       const uint32_t mask = hi_bits >= 32 ? 0xFFFFFFFFu : ((1u << hi_bits) - 1u);
       sticky |= (w[k] & mask);
@@ -490,18 +500,27 @@ __device__ inline double fixed_to_double(const uint32_t w[8]) {
   return __builtin_amdgcn_ldexp(static_cast<double>(mant), exp2 - 128);
 }
 
+// The step's gate.  Skip when the check is on and any element of the global
+// gradient is non-finite.  Otherwise the clip coefficient: 1 without
+// clipping; 0 when clipping and a non-finite element makes the global norm
+// infinite (max_norm / (inf + 1e-6)); else max_norm / (norm + 1e-6) in
+// binary64, clamped to 1 and rounded once to binary32.
 __device__ inline Gate evaluate_gate(const zero_norm_acc* accs, int n_accs, double max_norm,
                                      int check_overflow) {
   Gate g{1.0f, 0};
   if (n_accs <= 0 || accs == nullptr) return g;
-  uint32_t w[8];
-  uint64_t nonfinite, overflow;
-  acc_total(accs, n_accs, w, nonfinite, overflow);
-  if (check_overflow && (nonfinite + overflow) > 0) {
+  uint32_t w[kSumWords];
+  uint64_t nonfinite;
+  acc_total(accs, n_accs, w, nonfinite);
+  if (check_overflow && nonfinite > 0) {
     g.skip = 1;
     return g;
   }
   if (max_norm > 0.0) {
+    if (nonfinite > 0) {
+      g.coef = 0.0f;
+      return g;
+    }
     const double sumsq = fixed_to_double(w);
     const double norm = __builtin_sqrt(sumsq);
     const double denom = norm + 1e-6;

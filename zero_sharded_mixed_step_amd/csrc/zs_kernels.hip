@@ -15,17 +15,13 @@ namespace zs {
 
 // ---------------------------------------------------------------- grid ----
 
-static int g_cu_count[64];
-
+// Queried per launch (the runtime answers from its own device table), so the
+// library keeps no state between calls.
 int compute_units(int device) {
-  if (device < 0 || device >= 64) return 256;
-  int v = __atomic_load_n(&g_cu_count[device], __ATOMIC_RELAXED);
-  if (v > 0) return v;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  __atomic_store_n(&g_cu_count[device], cus, __ATOMIC_RELAXED);
   return cus;
 }
 
@@ -83,8 +79,11 @@ struct ReduceParams {
 // clears them; the launch boundary orders the two, so neither needs a
 // fence (an agent-scope fence per workgroup, which writes back L2, made the
 // pass four times slower).
-constexpr int kReduceSlots = ZERO_REDUCE_WORKSPACE_BYTES / 64;
-static_assert(kReduceSlots >= kThreads && sizeof(zero_norm_acc) == 64, "workspace layout");
+constexpr int kReduceSlots = ZERO_REDUCE_WORKSPACE_BYTES / sizeof(zero_norm_acc);
+static_assert(kReduceSlots == 512 && kReduceSlots >= kThreads, "workspace layout");
+
+// Norm totals of a workgroup: the kDigits digits, then the non-finite count.
+constexpr int kTot = kDigits + 1;
 
 // Sum over the 64 lanes of a wave (every lane receives it).
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
@@ -93,43 +92,47 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// Per-workgroup totals of a norm state (7 digits from the lanes' own LDS
-// rows, the non-finite and overflow counts from registers), reduced across
-// the workgroup by wave shuffles and one LDS exchange: every lane gets them
-// in tot[].  Ends with the workgroup past a barrier.
+// Per-workgroup totals of a norm state (the digits from the lanes' own LDS
+// rows, the non-finite count from a register), reduced across the workgroup
+// by wave shuffles and one LDS exchange: every lane gets them in tot[].  A
+// digit that is zero in every lane of a wave (most of them: a gradient's
+// group sums span a few binades) skips its shuffles; the ballot is uniform
+// across the wave.  Ends with the workgroup past a barrier.
 __device__ __forceinline__ void workgroup_norm_totals(const uint64_t (*s_digit)[kThreads],
-                                                      uint64_t extra0, uint64_t extra1,
-                                                      uint64_t (*s_part)[9], uint64_t tot[9]) {
+                                                      uint64_t count,
+                                                      uint64_t (*s_part)[kTot],
+                                                      uint64_t tot[kTot]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint64_t v[9];
+  uint64_t v[kTot];
 #pragma unroll
-  for (int k = 0; k < 7; ++k) v[k] = s_digit[k][tid];  // this lane's own row
-  v[7] = extra0;
-  v[8] = extra1;
+  for (int k = 0; k < kDigits; ++k) v[k] = s_digit[k][tid];  // this lane's own row
+  v[kDigits] = count;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) v[k] = wave_sum_u64(v[k]);
+  for (int k = 0; k < kTot; ++k)
+    if (__builtin_amdgcn_ballot_w64(v[k] != 0) != 0) v[k] = wave_sum_u64(v[k]);
   if (lane == 0) {
 #pragma unroll
-    for (int k = 0; k < 9; ++k) s_part[wave][k] = v[k];
+    for (int k = 0; k < kTot; ++k) s_part[wave][k] = v[k];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
+  for (int k = 0; k < kTot; ++k) {
     uint64_t t = 0;
     for (int w = 0; w < kThreads / 64; ++w) t += s_part[w][k];
     tot[k] = t;
   }
 }
 
-// Adds totals (7 digits, counts) to an accumulator; zero parts are skipped.
-__device__ __forceinline__ void acc_add(zero_norm_acc* acc, const uint64_t tot[9]) {
+// Adds totals (digits, count) to an accumulator; zero parts are skipped.
+__device__ __forceinline__ void acc_add(zero_norm_acc* acc, const uint64_t tot[kTot]) {
 #pragma unroll
-  for (int k = 0; k < 7; ++k)
+  for (int k = 0; k < kDigits; ++k)
     if (tot[k] != 0)
       atomicAdd(reinterpret_cast<unsigned long long*>(&acc->digit[k]),
                 static_cast<unsigned long long>(tot[k]));
-  if (tot[7] != 0) atomicAdd(&acc->nonfinite, static_cast<uint32_t>(tot[7]));
-  if (tot[8] != 0) atomicAdd(&acc->overflow, static_cast<uint32_t>(tot[8]));
+  if (tot[kDigits] != 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(&acc->nonfinite),
+              static_cast<unsigned long long>(tot[kDigits]));
 }
 
 #ifndef ZS_REDUCE_LOADS
@@ -162,15 +165,15 @@ template <int DT, int PT, bool WRITE, bool NORM, bool PIPE, bool ONESHOT>
 __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm) {
   static_assert(!PIPE || PT >= 4, "the pipelined fast path is built for 4 or 8 replicas");
   static_assert(!(PIPE && ONESHOT), "one loop form per kernel");
-  __shared__ uint64_t s_digit[NORM ? 7 : 1][kThreads];
-  __shared__ uint32_t s_count[(NORM && !ONESHOT) ? 2 : 1][kThreads];
+  __shared__ uint64_t s_digit[NORM ? kDigits : 1][kThreads];
+  __shared__ uint32_t s_count[(NORM && !ONESHOT) ? kThreads : 1];
   const int tid = threadIdx.x;
   const int quad_lane = tid & 3;
   if constexpr (NORM) {
 #pragma unroll
-    for (int k = 0; k < 7; ++k) s_digit[k][tid] = 0;
+    for (int k = 0; k < kDigits; ++k) s_digit[k][tid] = 0;
   }
-  uint32_t nonfinite = 0, overflow = 0;
+  uint32_t nonfinite = 0;
   // Averaged-gradient stores of whole tiles.  A lane owns 32 contiguous bytes
   // of g, so two per-lane 16-byte stores would each leave holes across the
   // wave; staging the wave's 2 KB in LDS lets every store instruction write
@@ -193,7 +196,6 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
   auto norm_chunk = [&](const float g[kVec]) {
     const double a = chunk_sumsq(g, nonfinite);
     const double S = quad_group_sum(a);
-    if (quad_lane == 0 && S >= 18446744073709551616.0) ++overflow;
     int d;
     uint64_t piece;
     fixed_point_piece(S, quad_lane, d, piece);
@@ -208,7 +210,6 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
     if ((u & 3) != 3) return;
     const double S = quad_lane == 0 ? s4[0] : (quad_lane == 1 ? s4[1]
                                             : (quad_lane == 2 ? s4[2] : s4[3]));
-    if (S >= 18446744073709551616.0) ++overflow;
     int base;
     uint32_t p0, p1, p2;
     fixed_point_split(S, base, p0, p1, p2);
@@ -306,34 +307,28 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
   }
   if constexpr (NORM && ONESHOT) {
     // Workgroup totals into slot blockIdx % kReduceSlots.
-    __shared__ uint64_t s_part[kThreads / 64][9];
-    uint64_t tot[9];
-    workgroup_norm_totals(s_digit, nonfinite, overflow, s_part, tot);
+    __shared__ uint64_t s_part[kThreads / 64][kTot];
+    uint64_t tot[kTot];
+    workgroup_norm_totals(s_digit, nonfinite, s_part, tot);
     if (tid == 0) acc_add(prm.slots + blockIdx.x % kReduceSlots, tot);
   } else if constexpr (NORM) {
-  s_count[0][tid] = nonfinite;
-  s_count[1][tid] = overflow;
-  __syncthreads();
-  for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
-    if (tid < stride) {
-#pragma unroll
-      for (int k = 0; k < 7; ++k) s_digit[k][tid] += s_digit[k][tid + stride];
-      s_count[0][tid] += s_count[0][tid + stride];
-      s_count[1][tid] += s_count[1][tid + stride];
-    }
+    s_count[tid] = nonfinite;
     __syncthreads();
-  }
-  if (tid == 0) {
-    zero_norm_acc* acc = prm.acc;
+    for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
+      if (tid < stride) {
 #pragma unroll
-    for (int k = 0; k < 7; ++k) {
-      const uint64_t v = s_digit[k][0];
-      if (v != 0) atomicAdd(reinterpret_cast<unsigned long long*>(&acc->digit[k]),
-                            static_cast<unsigned long long>(v));
+        for (int k = 0; k < kDigits; ++k) s_digit[k][tid] += s_digit[k][tid + stride];
+        s_count[tid] += s_count[tid + stride];
+      }
+      __syncthreads();
     }
-    if (s_count[0][0] != 0) atomicAdd(&acc->nonfinite, s_count[0][0]);
-    if (s_count[1][0] != 0) atomicAdd(&acc->overflow, s_count[1][0]);
-  }
+    if (tid == 0) {
+      uint64_t tot[kTot];
+#pragma unroll
+      for (int k = 0; k < kDigits; ++k) tot[k] = s_digit[k][0];
+      tot[kDigits] = s_count[0];
+      acc_add(prm.acc, tot);
+    }
   }
 }
 
@@ -341,22 +336,23 @@ __global__ void __launch_bounds__(kThreads) shard_reduce_kernel(ReduceParams prm
 // workgroup; each slot field is read and cleared by one atomic exchange).
 __global__ void __launch_bounds__(kThreads) slot_fold_kernel(zero_norm_acc* slots,
                                                              zero_norm_acc* acc) {
-  __shared__ uint64_t s_rows[7][kThreads];
-  __shared__ uint64_t s_part[kThreads / 64][9];
+  __shared__ uint64_t s_rows[kDigits][kThreads];
+  __shared__ uint64_t s_part[kThreads / 64][kTot];
   const int tid = threadIdx.x;
-  uint64_t mine[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  uint64_t mine[kTot];
+#pragma unroll
+  for (int k = 0; k < kTot; ++k) mine[k] = 0;
   for (int sl = tid; sl < kReduceSlots; sl += kThreads) {
     zero_norm_acc* a = slots + sl;
 #pragma unroll
-    for (int k = 0; k < 7; ++k)
+    for (int k = 0; k < kDigits; ++k)
       mine[k] += atomicExch(reinterpret_cast<unsigned long long*>(&a->digit[k]), 0ull);
-    mine[7] += atomicExch(&a->nonfinite, 0u);
-    mine[8] += atomicExch(&a->overflow, 0u);
+    mine[kDigits] += atomicExch(reinterpret_cast<unsigned long long*>(&a->nonfinite), 0ull);
   }
 #pragma unroll
-  for (int k = 0; k < 7; ++k) s_rows[k][tid] = mine[k];
-  uint64_t tot[9];
-  workgroup_norm_totals(s_rows, mine[7], mine[8], s_part, tot);
+  for (int k = 0; k < kDigits; ++k) s_rows[k][tid] = mine[k];
+  uint64_t tot[kTot];
+  workgroup_norm_totals(s_rows, mine[kDigits], s_part, tot);
   if (tid == 0) acc_add(acc, tot);
 }
 

@@ -135,19 +135,23 @@ class ShardStep:
         if self.path == "fused":
             return
         for lo, hi in self._ranges():
-            ws = self.reduce_ws if hi - lo > self.oneshot_min else None
+            g = self.g[lo:hi] if self.path == "materialize" else None
+            oneshot = hi - lo > self.oneshot_min
             if self.mx_grads:
                 codes = [c[lo:hi] for c, _ in replicas]
                 scales = [sc[lo // 32:hi // 32] for _, sc in replicas]
-                B.zero_shard_reduce_mx(codes, scales, self.inv_scale, g_out=self.g[lo:hi],
-                                       acc=self.acc, workspace=ws)
+                if oneshot:
+                    B.zero_shard_reduce_mx_ws(codes, scales, self.inv_scale, self.reduce_ws,
+                                              g_out=g, acc=self.acc)
+                else:
+                    B.zero_shard_reduce_mx(codes, scales, self.inv_scale, g_out=g, acc=self.acc)
                 continue
             views = [r[lo:hi] for r in replicas]
-            if self.path == "materialize":
-                B.zero_shard_reduce(views, self.inv_scale, g_out=self.g[lo:hi], acc=self.acc,
-                                    workspace=ws)
+            if oneshot:
+                B.zero_shard_reduce_ws(views, self.inv_scale, self.reduce_ws, g_out=g,
+                                       acc=self.acc)
             else:
-                B.zero_shard_reduce(views, self.inv_scale, acc=self.acc, workspace=ws)
+                B.zero_shard_reduce(views, self.inv_scale, g_out=g, acc=self.acc)
 
     def _resolve_pending_skip(self) -> None:
         if self._skip_event is not None:
@@ -158,7 +162,7 @@ class ShardStep:
 
     def update(self, replicas: Optional[List[torch.Tensor]] = None,
                accs: Optional[torch.Tensor] = None) -> None:
-        """AdamW on the shard; `accs` (k, 8) replaces the own accumulator when
+        """AdamW on the shard; `accs` (k, 16) replaces the own accumulator when
         the global norm state includes other ranks."""
         self._resolve_pending_skip()
         kw = dict(step=self.t + 1, lr=self.lr, beta1=self.beta1, beta2=self.beta2,
