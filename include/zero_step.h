@@ -171,6 +171,24 @@ int zero_shard_reduce_mx_ws(const uint8_t *const *codes, const uint8_t *const *s
                             zero_norm_acc *acc, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* The same reduce as zero_shard_reduce_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the 512 norm slots live in a static
+ * device array of this library (ZERO_REDUCE_WORKSPACE_BYTES = 64 KiB per
+ * GPU, held from the first call on that GPU until the process ends) instead
+ * of a caller workspace.  Nothing is allocated: the first call on a device,
+ * with that device current, looks up that device's address of the array;
+ * every call clears the slots with a fill kernel before the reduce and the
+ * fold leaves them zero.  The array is not sized by n: n is limited only as
+ * for every norm call (n <= 2^37, ZERO_ESIZE beyond).  All calls on one GPU
+ * share the array, so calls that overlap on one GPU (concurrent streams,
+ * host threads) race and give wrong norms: order them on one stream.
+ * Arguments, results and status codes otherwise as zero_shard_reduce; the
+ * results are bitwise those of zero_shard_reduce_ws. */
+int zero_shard_reduce_noalloc(const void *const *replicas, int P, int dtype, size_t n,
+                              float inv_scale, float *g_out, zero_norm_acc *acc,
+                              void *stream);
+
 /* Norm state of one buffer: adds the groups of g[i] = grad[i] * inv_scale
  * (grad fp32 or bf16, device) to acc, as zero_shard_reduce with P = 1 and
  * no output.  Used for a single replica (P = 1) or a materialised gradient

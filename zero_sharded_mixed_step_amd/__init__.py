@@ -11,7 +11,7 @@ from ._binding import (REDUCE_WORKSPACE_BYTES, ZERO_BF16, ZERO_F32,  # noqa: F40
                        new_reduce_workspace, read_norm_acc, zero_abi_version, zero_adamw_step,
                        zero_adamw_step_unfused, zero_grad_norm, zero_inv_scale, zero_mxfp8_pack,
                        zero_norm_acc_clear, zero_shard_reduce, zero_shard_reduce_mx,
-                       zero_shard_reduce_mx_ws, zero_shard_reduce_ws,
+                       zero_shard_reduce_mx_ws, zero_shard_reduce_noalloc, zero_shard_reduce_ws,
                        zero_step_gate,
                        zero_strerror,
                        zero_unfused_workspace_bytes)

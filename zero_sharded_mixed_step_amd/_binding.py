@@ -57,6 +57,7 @@ def lib():
         L.zero_norm_acc_clear.argtypes = [vp, i, vp]
         L.zero_shard_reduce.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp]
         L.zero_shard_reduce_ws.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp, sz, vp]
+        L.zero_shard_reduce_noalloc.argtypes = [vp, i, i, sz, C.c_float, vp, vp, vp]
         L.zero_grad_norm.argtypes = [vp, i, sz, C.c_float, vp, vp]
         L.zero_adamw_step.argtypes = [C.POINTER(_AdamArgs), vp]
         L.zero_step_gate.argtypes = [vp, i, C.c_double, i, vp, vp, vp]
@@ -67,6 +68,7 @@ def lib():
         L.zero_unfused_workspace_bytes.restype = sz
         L.zero_adamw_step_unfused.argtypes = [C.POINTER(_AdamArgs), vp, sz, vp]
         for f in (L.zero_norm_acc_clear, L.zero_shard_reduce, L.zero_shard_reduce_ws,
+                  L.zero_shard_reduce_noalloc,
                   L.zero_shard_reduce_mx, L.zero_shard_reduce_mx_ws, L.zero_grad_norm,
                   L.zero_adamw_step, L.zero_step_gate, L.zero_mxfp8_pack,
                   L.zero_adamw_step_unfused):
@@ -231,6 +233,17 @@ def zero_shard_reduce_ws(replicas, inv_scale: float, workspace, g_out=None, acc=
                                       _dtype_code(reps[0]), n, float(inv_scale),
                                       _dev_ptr(g_out, "g_out"), ap, wp, wb, _stream(stream)),
            "zero_shard_reduce_ws")
+
+
+def zero_shard_reduce_noalloc(replicas, inv_scale: float, g_out=None, acc=None, n=None,
+                              stream=None) -> None:
+    """zero_shard_reduce_ws with the library's own static slots (no
+    workspace, nothing allocated); calls on one GPU must not overlap."""
+    reps, n, ap = _reduce_args(replicas, n, g_out, acc, "zero_shard_reduce_noalloc")
+    _check(lib().zero_shard_reduce_noalloc(_ptr_array(reps, "replica"), len(reps),
+                                           _dtype_code(reps[0]), n, float(inv_scale),
+                                           _dev_ptr(g_out, "g_out"), ap, _stream(stream)),
+           "zero_shard_reduce_noalloc")
 
 
 def _mx_args(codes, scales, n, g_out, acc, name):

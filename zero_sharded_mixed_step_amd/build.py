@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzero_step.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("zs_kernels.hip", "zs_unfused.hip", "zs_abi.hip")]
+           for f in ("zs_kernels.hip", "zs_unfused.hip", "zs_abi.hip", "zs_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
