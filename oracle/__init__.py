@@ -156,12 +156,13 @@ def _ptr_array(arrs):
     return (C.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
 
 
-def reduce(replicas, inv_scale_f: float) -> np.ndarray:
+def reduce(replicas, inv_scale_f: float, out: np.ndarray = None) -> np.ndarray:
     reps = [np.ascontiguousarray(r) for r in replicas]
     n = reps[0].size
     code = _dtype_code(reps[0])
     assert all(r.size == n and r.dtype == reps[0].dtype for r in reps)
-    g = np.empty(n, dtype=np.float32)
+    g = np.empty(n, dtype=np.float32) if out is None else out
+    assert g.dtype == np.float32 and g.size == n and g.flags["C_CONTIGUOUS"]
     lib().oracle_reduce(_ptr_array(reps), len(reps), code, n, inv_scale_f, _ptr(g))
     return g
 

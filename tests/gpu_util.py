@@ -1,7 +1,9 @@
-"""Helpers of the GPU parity tests: device transfer of numpy arrays and the
-streaming oracle (inputs regenerated on the host from the counter-based
-generator, chunk by chunk, across threads; the oracle does all arithmetic)."""
+"""Helpers of the GPU parity tests: device transfer of numpy arrays, the
+oracle over whole workloads (inputs regenerated on the host from the
+counter-based generator, chunk by chunk, across threads; the oracle does all
+arithmetic), and full comparisons of device state with it."""
 import os
+import time
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -83,3 +85,123 @@ def oracle_norm_parallel(workload, call, lo, hi, threads=THREADS):
     for p in parts:
         O.acc_add(total, p)
     return total
+
+
+def log(msg):
+    """Progress line of a long parity test (shown with pytest -s)."""
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def _chunks(n, chunk):
+    return [(a, min(n, a + chunk)) for a in range(0, n, chunk)]
+
+
+class OracleRun:
+    """The oracle following a workload's whole step schedule on elements
+    [lo, lo + n) of the flat vector (one rank's shard, or the whole vector of
+    all ranks), with the whole state in host memory: master, m, v, param and
+    one call's averaged gradient.  Each call regenerates that call's gradient
+    replicas chunk by chunk (never all of them at once), reduces them into
+    the gradient and adds the chunk's norm state (32-aligned chunks, integer
+    sums: the split changes nothing); then the gate of the global state, then
+    AdamW chunk by chunk.  Every arithmetic step is an oracle call; threads
+    only spread the chunks."""
+
+    def __init__(self, w, lo, n, threads=THREADS, chunk=1 << 22):
+        assert lo % 32 == 0 and chunk % 32 == 0
+        self.w, self.lo, self.n, self.threads = w, lo, n, threads
+        self.cuts = _chunks(n, chunk)
+        self.ex = ThreadPoolExecutor(threads)
+        self.master = synth.fill(w.master_spec(), lo, n, False, threads=threads)
+        self.m = np.zeros(n, np.float32)
+        self.v = np.zeros(n, np.float32)
+        self.param = np.empty(n, np.uint16)
+        self.g = np.empty(n, np.float32)
+        self.inv = O.inv_scale(w.P, w.loss_scale)
+        self.t = 0
+        self.gates = []                      # (call, skip, coef, acc) per call
+
+        def init(c):
+            a, b = c
+            self.param[a:b] = O.f32_to_bf16(self.master[a:b])
+        list(self.ex.map(init, self.cuts))
+
+    def _grad_chunk(self, call, c):
+        w = self.w
+        a, b = c
+        s = self.lo + a
+        reps = [synth.fill(w.grad_spec(call, k), s, b - a, w.grad_bf16) for k in range(w.P)]
+        if w.inject and w.inject[0] == call and s <= w.inject[1] < s + (b - a):
+            reps[0][w.inject[1] - s] = 0x7F80 if w.grad_bf16 else np.float32(np.inf)
+        if w.mx_grads:                       # MXFP8-stored replicas: pack, then decode
+            reps = [O.mxfp8_decode(*O.mxfp8_pack(r)) for r in reps]
+        O.reduce(reps, self.inv, out=self.g[a:b])
+        return O.norm_accumulate(self.g[a:b])
+
+    def call(self, call, extra_accs=()):
+        """One call of the schedule; `extra_accs`: norm states of elements
+        outside [lo, lo + n) that belong to the same global norm."""
+        w = self.w
+        acc = O.acc_zero()
+        for part in self.ex.map(lambda c: self._grad_chunk(call, c), self.cuts):
+            O.acc_add(acc, part)
+        glob = acc.copy()
+        for e in extra_accs:
+            O.acc_add(glob, e)
+        skip, coef = O.gate(glob, w.max_norm, w.check_overflow)
+        self.gates.append((call, skip, coef, acc))
+        if skip:
+            return skip, coef, acc
+        self.t += 1
+        s = O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, self.t)
+
+        def upd(c):
+            a, b = c
+            O.adamw(self.g[a:b], coef, s, self.master[a:b], self.m[a:b], self.v[a:b],
+                    self.param[a:b])
+        list(self.ex.map(upd, self.cuts))
+        return skip, coef, acc
+
+    def mxfp8(self):
+        """The oracle's MXFP8 pack of the current param, chunk by chunk."""
+        elem = np.empty(self.n, np.uint8)
+        scale = np.empty(self.n // 32, np.uint8)
+
+        def pack(c):
+            a, b = c
+            elem[a:b], scale[a // 32:b // 32] = O.mxfp8_pack(self.param[a:b])
+        list(self.ex.map(pack, self.cuts))
+        return elem, scale
+
+    def close(self):
+        self.ex.shutdown()
+
+
+def compare_full(name, dev, host, lo=0, chunk=1 << 26, bf16=False, threads=THREADS):
+    """Every element of a device tensor against a host array, copied back in
+    chunks: returns (count of non-identical elements, max relative error,
+    first differing index or None).  A reference of 0 needs an exact 0."""
+    n = host.size
+    cuts = _chunks(n, chunk)
+
+    def part(c):
+        a, b = c
+        got = from_dev(dev[lo + a:lo + b], bf16)
+        want = host[a:b]
+        diff = got.view(np.uint8).reshape(b - a, -1) != want.view(np.uint8).reshape(b - a, -1)
+        bad = np.nonzero(diff.any(axis=1))[0]
+        if bad.size == 0:
+            return 0, 0.0, None
+        gv = got[bad].astype(np.float64) if not bf16 else O.bf16_to_f32(got[bad]).astype(np.float64)
+        wv = want[bad].astype(np.float64) if not bf16 else O.bf16_to_f32(want[bad]).astype(np.float64)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            rel = np.where(wv != 0, np.abs(gv - wv) / np.abs(wv), np.inf)
+        return int(bad.size), float(np.nanmax(rel)), a + int(bad[0])
+
+    with ThreadPoolExecutor(min(threads, 8)) as ex:
+        res = list(ex.map(part, cuts))
+    nbad = sum(r[0] for r in res)
+    worst = max(r[1] for r in res)
+    first = next((r[2] for r in res if r[2] is not None), None)
+    log(f"{name}: {n} elements, {nbad} non-identical, max rel err {worst:.3e}")
+    return nbad, worst, first

@@ -1,27 +1,34 @@
-"""Parity at the five workloads' real sizes, in the launch configuration the
-benchmark times (ShardStep with the workload's bucket, gate and pack
-settings).
+"""Parity at the workloads' real sizes over their whole schedules, in the
+launch configuration the benchmark times (ShardStep with the workload's
+bucket, gate and pack settings, the device step counter).
 
-  - 1M-element, P=4 fp32 case and the GPT-2-small-sized P=8 case: every
-    element of every rank compared with the oracle; the P=8 case also checks
-    that the 8 shard steps equal one unsharded step of the full vector on the
-    GPU (reduce-scatter + all-gather = all-reduce).
-  - 1.3B, 7B and 30B cases: the oracle computes each call's global norm and
-    overflow count over the whole shard (inputs regenerated on the host from
-    the counter-based generator, spread over threads), then follows sampled
-    elements (random indices plus tile, bucket and tail boundaries) through
-    every call; the GPU state at those indices must match bit for bit.  The
-    30B case also checks the MXFP8 pack of sampled 32-element blocks.
-Step counts of the three large cases are cut (noted per test) to keep the host
-side of the oracle within a couple of minutes.
+Every element of the final state is compared with the oracle, bit for bit:
+master, m, v and the bf16 param (and the MXFP8 pack where the workload packs),
+with the count of non-identical elements and the max relative error reported.
+The global norm state of every call (the accumulator the device gate reads)
+is compared bit for bit too, call by call.  The oracle holds the whole state
+in host memory and regenerates each call's gradient replicas chunk by chunk
+from the counter-based generator (OracleRun).
+
+  - 1M-element P=4 fp32 case: every rank, one step.
+  - GPT-2-small-sized P=8 case: all 8 ranks over 10 steps against the oracle
+    on the whole vector (each rank's norm state added into the global one,
+    the norm all-reduce), and the 8 shard steps against one unsharded
+    step of the full vector on the GPU.
+  - 1.3B unsharded (10 calls, loss scale, an injected inf at call 5 that is
+    skipped), 7B shard (10 steps, 35 buckets of 25M, clip), 30B shard (5
+    steps, clip + overflow check, MXFP8 pack fused, then the standalone
+    pack): whole schedules, every element.
+  - 30B shard with MXFP8-stored gradient replicas: the host packs and
+    decodes all 8 replicas of every chunk at every call, which is what
+    bounds its length (the first two of its five calls).
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import synth
-from gpu_util import (from_dev, gpu_or_skip, mismatch_report, oracle_norm_parallel,
-                      same_bits)
+from gpu_util import OracleRun, compare_full, from_dev, gpu_or_skip, log, same_bits
 from synth import configs
 
 pytestmark = pytest.mark.gpu
@@ -75,21 +82,24 @@ def _init_state(st, w, lo):
     synth.fill_device(w.master_spec(), lo, st.param)
 
 
-def _host_replicas(w, call, lo, n):
-    reps = [synth.fill(w.grad_spec(call, k), lo, n, w.grad_bf16, threads=8) for k in range(w.P)]
-    if w.inject and w.inject[0] == call and lo <= w.inject[1] < lo + n:
-        reps[0][w.inject[1] - lo] = 0x7F80 if w.grad_bf16 else np.float32(np.inf)
-    return reps
+def _acc_sum(zs, accs):
+    """(X, nonfinite) of the sum of device accumulators."""
+    rows = zs.read_norm_acc(accs)
+    return sum(r[0] for r in rows), sum(r[1] for r in rows)
 
 
-def _compare_state(st, want, where=""):
-    names = ("master", "m", "v", "param")
-    got = (from_dev(st.master), from_dev(st.m), from_dev(st.v), from_dev(st.param, True))
-    for name, g, h in zip(names, got, want):
-        assert same_bits(g, h), mismatch_report(f"{where} {name}", g, h)
+def _assert_state(st, run, where):
+    """Every element of master/m/v/param of the device step `st` against the
+    oracle run."""
+    host = {"master": run.master, "m": run.m, "v": run.v, "param": run.param}
+    for name in ("master", "m", "v", "param"):
+        nbad, rel, first = compare_full(f"{where} {name}", getattr(st, name), host[name],
+                                        bf16=name == "param")
+        assert nbad == 0, f"{where} {name}: {nbad} elements differ (first at {first}), " \
+                          f"max rel err {rel:.3e}"
 
 
-# -------------------------------------------------------------- full ones --
+# -------------------------------------------------------------- small ones --
 
 def test_flat_1m_p4_fp32_all_ranks(zs):
     import torch
@@ -105,30 +115,29 @@ def test_flat_1m_p4_fp32_all_ranks(zs):
         master = synth.fill(w.master_spec(), lo, w.S, False)
         m, v = np.zeros(w.S, np.float32), np.zeros(w.S, np.float32)
         param = O.f32_to_bf16(master)
-        hreps = _host_replicas(w, 1, lo, w.S)
+        hreps = [synth.fill(w.grad_spec(1, k), lo, w.S, False) for k in range(w.P)]
         skipped, _ = O.step(hreps, O.inv_scale(w.P, 1.0), 0.0, False, w.lr, w.beta1, w.beta2,
                             w.eps, w.wd, 1, master, m, v, param)
         assert not skipped
-        _compare_state(st, (master, m, v, param), f"rank {rank}")
+        for name, want in (("master", master), ("m", m), ("v", v), ("param", param)):
+            got = from_dev(getattr(st, name), name == "param")
+            assert same_bits(got, want), f"rank {rank} {name}"
 
 
 @pytest.mark.timeout(900)
 def test_gpt2_small_p8_ten_steps_all_ranks(zs):
+    """All 8 ranks over the 10 steps against the oracle on the whole vector,
+    and the 8 shard steps against one unsharded GPU step."""
     import torch
     w = configs.GPT2_SMALL
-    ranks = [_step_for(zs, w) for _ in range(w.P)]
+    ranks = [_step_for(zs, w, device_counter=True) for _ in range(w.P)]
     for r, st in enumerate(ranks):
         _init_state(st, w, r * w.S)
-    # unsharded reference on the GPU: one rank holding the whole vector
-    full = _step_for(zs, w, n=w.N, path="materialize")
+    full = _step_for(zs, w, n=w.N, path="materialize", device_counter=True)
     _init_state(full, w, 0)
     accs = zs.new_norm_acc(w.P)
     reps = None
-    # oracle: rank 0 in full, global norm from all ranks
-    master = synth.fill(w.master_spec(), 0, w.S, False)
-    m, v = np.zeros(w.S, np.float32), np.zeros(w.S, np.float32)
-    param = O.f32_to_bf16(master)
-    inv = O.inv_scale(w.P, 1.0)
+    per_call = []
     for call in range(1, w.steps + 1):
         reps = _device_replicas(w, call, 0, w.N, out=reps)
         for r, st in enumerate(ranks):
@@ -136,146 +145,108 @@ def test_gpt2_small_p8_ten_steps_all_ranks(zs):
             accs[r].copy_(st.acc[0])
         for r, st in enumerate(ranks):
             st.update([x[r * w.S:(r + 1) * w.S] for x in reps], accs=accs)
-        full.reduce(reps)
-        full.update(reps)
-        rest = oracle_norm_parallel(w, call, w.S, w.N)
-        skipped, _ = O.step(_host_replicas(w, call, 0, w.S), inv, w.max_norm, w.check_overflow,
-                            w.lr, w.beta1, w.beta2, w.eps, w.wd, call, master, m, v, param,
-                            extra_accs=[rest])
-        assert not skipped
+        full.step(reps)
+        per_call.append(accs.clone())
     torch.cuda.synchronize()
-    _compare_state(ranks[0], (master, m, v, param), "rank 0 vs oracle")
     for name in ("master", "m", "v", "param"):
         cat = torch.cat([getattr(st, name) for st in ranks])
         assert torch.equal(cat, getattr(full, name)), f"sharded != unsharded: {name}"
+    del reps
+    log(f"{w.name}: GPU done, oracle over all {w.N} elements")
+    run = OracleRun(w, 0, w.N)
+    try:
+        for call in range(1, w.steps + 1):
+            skip, _, acc = run.call(call)
+            assert not skip
+            assert _acc_sum(zs, per_call[call - 1]) == (acc.X, int(acc.nonfinite)), call
+        assert [st.applied_steps() for st in ranks] == [w.steps] * w.P
+        for r, st in enumerate(ranks):
+            sl = slice(r * w.S, (r + 1) * w.S)
+            for name, host in (("master", run.master), ("m", run.m), ("v", run.v),
+                               ("param", run.param)):
+                nbad, rel, first = compare_full(f"rank {r} {name}", getattr(st, name),
+                                                np.ascontiguousarray(host[sl]),
+                                                bf16=name == "param")
+                assert nbad == 0, f"rank {r} {name}: {nbad} differ (first {first}), rel {rel:.3e}"
+    finally:
+        run.close()
 
 
-# ----------------------------------------------------------- sampled ones --
+# ------------------------------------------------------- full-size ones --
 
-def _sample_indices(w, rng, k=4096):
-    S = w.S
-    idx = set(int(i) for i in rng.integers(0, S, size=k))
-    marks = [0, 1, 7, 8, 31, 32, 2047, 2048, S - 33, S - 32, S - 1]
-    if w.bucket:
-        for b in range(w.bucket, S, w.bucket):
-            marks += [b - 1, b]
-    if w.inject:
-        marks += [w.inject[1] - 1, w.inject[1], w.inject[1] + 1]
-    idx.update(i for i in marks if 0 <= i < S)
-    idx = np.array(sorted(idx), dtype=np.uint64)
-    if w.mx_grads:
-        # whole 32-element blocks: a decoded element depends on its block
-        blocks = np.unique(idx // np.uint64(32))
-        idx = (blocks[:, None] * np.uint64(32) + np.arange(32, dtype=np.uint64)[None, :]).ravel()
-    return idx
-
-
-def _oracle_gates(w, calls):
-    gates = []
-    for call in calls:
-        acc = oracle_norm_parallel(w, call, w.shard_start(), w.shard_start() + w.S)
-        skip, coef = O.gate(acc, w.max_norm, w.check_overflow)
-        gates.append((coef, skip))
-    return gates
-
-
-def _oracle_samples(w, idx, calls, gates):
-    gidx = idx + np.uint64(w.shard_start())
-    master = synth.gather(w.master_spec(), gidx, False)
-    m, v = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
-    param = O.f32_to_bf16(master)
-    inv = O.inv_scale(w.P, w.loss_scale)
-    t = 0
-    for call, (coef, skip) in zip(calls, gates):
-        if skip:
-            continue
-        t += 1
-        reps = [synth.gather(w.grad_spec(call, k), gidx, w.grad_bf16) for k in range(w.P)]
-        if w.inject and w.inject[0] == call:
-            hit = np.nonzero(gidx == np.uint64(w.inject[1]))[0]
-            for h in hit:
-                reps[0][h] = 0x7F80 if w.grad_bf16 else np.float32(np.inf)
-        if w.mx_grads:      # idx holds whole blocks, in order
-            reps = [O.mxfp8_decode(*O.mxfp8_pack(r)) for r in reps]
-        g = O.reduce(reps, inv)
-        O.adamw(g, coef, O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, t), master, m,
-                v, param)
-    return master, m, v, param, t
-
-
-def _run_sampled(zs, w, calls, seed):
+def _run_full(zs, w, calls, pack_checks=False):
+    """The workload's schedule on the GPU as the benchmark runs it (device
+    counter), the global norm state read after every call; then the oracle
+    over the whole shard and the comparison of every call's norm state and
+    every element of the final state."""
     import torch
-    rng = np.random.default_rng(seed)
-    idx = _sample_indices(w, rng)
-    st = _step_for(zs, w, device_counter=True)     # as the benchmark runs the step
+    st = _step_for(zs, w, device_counter=True)
     _init_state(st, w, w.shard_start())
     reps = None
+    dev_accs = []
     for call in calls:
         reps = _device_replicas(w, call, w.shard_start(), w.S, out=reps)
         st.step(reps)
+        dev_accs.append(st.acc.clone())
     applied = st.applied_steps()
     torch.cuda.synchronize()
-    di = torch.from_numpy(idx.astype(np.int64)).cuda()
-    got = (from_dev(st.master[di]), from_dev(st.m[di]), from_dev(st.v[di]),
-           from_dev(st.param[di], True))
     del reps
-    gates = _oracle_gates(w, calls)
-    want = _oracle_samples(w, idx, calls, gates)
-    assert applied == want[4], (applied, want[4])
-    for name, g, h in zip(("master", "m", "v", "param"), got, want[:4]):
-        assert same_bits(g, h), mismatch_report(f"{w.name} {name}", g, h)
-    return st, idx, gates
+    log(f"{w.name}: GPU done ({len(calls)} calls), oracle over {w.S} elements")
+    run = OracleRun(w, w.shard_start(), w.S)
+    try:
+        for call, dacc in zip(calls, dev_accs):
+            skip, coef, acc = run.call(call)
+            log(f"{w.name}: call {call}: skip {skip}, coef {coef!r}")
+            assert _acc_sum(zs, dacc) == (acc.X, int(acc.nonfinite)), f"norm state, call {call}"
+        assert applied == run.t, (applied, run.t)
+        _assert_state(st, run, w.name)
+        if pack_checks:
+            want_e, want_s = run.mxfp8()
+            assert st.fuse_pack
+            assert compare_full(f"{w.name} fused mxfp8 codes", st.mx_elem, want_e)[0] == 0
+            assert compare_full(f"{w.name} fused mxfp8 scales", st.mx_scale, want_s)[0] == 0
+            st.mx_elem.zero_()
+            st.mx_scale.zero_()
+            st.pack_param()                       # the standalone pack kernel
+            torch.cuda.synchronize()
+            assert compare_full(f"{w.name} mxfp8 codes", st.mx_elem, want_e)[0] == 0
+            assert compare_full(f"{w.name} mxfp8 scales", st.mx_scale, want_s)[0] == 0
+        return st, run
+    finally:
+        run.close()
 
 
 @pytest.mark.timeout(900)
 def test_1p3b_unsharded_loss_scale_skip(zs):
-    # calls 1..6 of 10: covers the injected overflow at call 5 and the
-    # applied step after it
     w = configs.UNSHARDED_1P3B
-    st, _, gates = _run_sampled(zs, w, calls=range(1, 7), seed=3)
-    assert [s for _, s in gates] == [False, False, False, False, True, False]
-    assert st.path == "recompute"
-    assert int(st.skipped.item()) == 0
+    st, run = _run_full(zs, w, calls=range(1, w.steps + 1))
+    assert [s for _, s, _, _ in run.gates] == [c == 5 for c in range(1, 11)]
+    assert st.path == "recompute" and run.t == 9
+    del st
 
 
 @pytest.mark.timeout(900)
 def test_7b_shard_35_buckets_clip(zs):
-    # 2 of the 10 steps at the full 875M shard, 35 buckets of 25M
     w = configs.SHARD_7B
-    st, _, _ = _run_sampled(zs, w, calls=range(1, 3), seed=4)
-    assert st.path == "materialize" and st.bucket == 25_000_000
+    st, run = _run_full(zs, w, calls=range(1, w.steps + 1))
+    assert st.path == "materialize" and st.bucket == 25_000_000 and run.t == w.steps
+    assert all(0 < c < 1 for _, _, c, _ in run.gates)       # the clip acts at every step
+    del st
 
 
 @pytest.mark.timeout(1200)
 def test_30b_shard_clip_overflow_then_mxfp8(zs):
-    # 2 of the 5 steps at the full 3.75B shard, then the MXFP8 pack
-    import torch
     w = configs.SHARD_30B
-    rng = np.random.default_rng(5)
-    st, idx, gates = _run_sampled(zs, w, calls=range(1, 3), seed=5)
-    blocks = np.unique(rng.integers(0, w.S // 32, size=256))
-    blocks = np.unique(np.concatenate([blocks, [0, w.S // 32 - 1]]))
-    eidx = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel().astype(np.uint64)
-    de = torch.from_numpy(eidx.astype(np.int64)).cuda()
-    ds = torch.from_numpy(blocks.astype(np.int64)).cuda()
-    assert st.fuse_pack
-    fused_e, fused_s = from_dev(st.mx_elem[de]), from_dev(st.mx_scale[ds])
-    st.pack_param()                       # the standalone pack kernel
-    torch.cuda.synchronize()
-    got_e, got_s = from_dev(st.mx_elem[de]), from_dev(st.mx_scale[ds])
-    _, _, _, param, _ = _oracle_samples(w, eidx, range(1, 3), gates)
-    want_e, want_s = O.mxfp8_pack(param)
-    for e, sc in ((fused_e, fused_s), (got_e, got_s)):
-        assert np.array_equal(sc, want_s)
-        assert np.array_equal(e, want_e)
+    st, run = _run_full(zs, w, calls=range(1, w.steps + 1), pack_checks=True)
+    assert run.t == w.steps
+    del st
 
 
 @pytest.mark.timeout(1200)
 def test_30b_shard_mxfp8_stored_grads(zs):
-    # 1 of the 5 steps at the full 3.75B shard: the host oracle packs and
-    # decodes all 8 replicas of the whole shard for the norm (~2 min on 16
-    # threads), so one call is what fits
+    # the first two of the five calls: the host packs and decodes every
+    # replica chunk of every call (8 x 3.75e9 elements per call)
     w = configs.SHARD_30B_MX
-    st, idx, gates = _run_sampled(zs, w, calls=range(1, 2), seed=6)
-    assert st.path == "materialize" and idx.size % 32 == 0
-    assert gates[0][1] is False
+    st, run = _run_full(zs, w, calls=range(1, 3))
+    assert st.path == "materialize" and run.t == 2
+    del st
