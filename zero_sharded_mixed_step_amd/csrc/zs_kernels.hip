@@ -479,7 +479,8 @@ struct AdamParams {
 // SRC < 0: gradient from prm.grad (fp32); otherwise the replica dtype.
 // MX: also pack the new bf16 params to MXFP8 (n % 32 == 0); the loop then
 // stays wave-uniform because the block amax is a quad DPP reduction.
-template <int SRC, int PT, bool PARAM, bool MX>
+// U: tiles per workgroup (one-shot grid).
+template <int SRC, int PT, bool PARAM, bool MX, int U>
 __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
   __shared__ Gate s_gate;
   __shared__ AdamScalars s_sc;
@@ -528,7 +529,6 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
       }
     }
   };
-  constexpr int U = ZS_ADAMW_UNROLL;
   const uint64_t ntiles = (prm.nchunks + kThreads - 1) / kThreads;
   const uint64_t full_tiles = prm.n / (static_cast<uint64_t>(kThreads) * kVec);
   const uint64_t step = static_cast<uint64_t>(gridDim.x) * U;
@@ -592,11 +592,20 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
   }
 }
 
+// ZS_ADAMW_UNROLL tiles per workgroup, except where that grid would leave
+// compute units idle (shards below about 2M elements): one tile each, twice
+// the workgroups.
 template <int SRC, int PT, bool PARAM, bool MX>
 static void adamw_launch(const AdamParams& prm, hipStream_t st) {
-  hipLaunchKernelGGL((adamw_kernel<SRC, PT, PARAM, MX>),
-                     dim3(grid_oneshot(prm.nchunks, ZS_ADAMW_UNROLL)), dim3(kThreads), 0, st,
-                     prm);
+  const unsigned g = grid_oneshot(prm.nchunks, ZS_ADAMW_UNROLL);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (g < 2u * static_cast<unsigned>(compute_units(dev)))
+    hipLaunchKernelGGL((adamw_kernel<SRC, PT, PARAM, MX, 1>), dim3(grid_oneshot(prm.nchunks, 1)),
+                       dim3(kThreads), 0, st, prm);
+  else
+    hipLaunchKernelGGL((adamw_kernel<SRC, PT, PARAM, MX, ZS_ADAMW_UNROLL>), dim3(g),
+                       dim3(kThreads), 0, st, prm);
 }
 
 template <int SRC, int PT>

@@ -74,7 +74,7 @@ class ShardStep:
                  bucket: Optional[int] = None, pack: bool = False,
                  fuse_pack: bool = True, path: Optional[str] = None,
                  device_counter: bool = False, oneshot_min: Optional[int] = None,
-                 device="cuda"):
+                 bucket_streams: int = 2, device="cuda"):
         self.n, self.P = int(n), int(P)
         self.lr, self.beta1, self.beta2, self.eps, self.wd = lr, beta1, beta2, eps, weight_decay
         self.max_norm, self.check_overflow = float(max_norm), bool(check_overflow)
@@ -103,6 +103,19 @@ class ShardStep:
         # reduce call (so a recorded graph replays without clearing it).
         self.reduce_ws = B.new_reduce_workspace(dev)
         self.oneshot_min = ONESHOT_MIN if oneshot_min is None else int(oneshot_min)
+        # Bucket reduces alternate over this many streams (same priority),
+        # joined before the update: a bucket's launch ramps up while the
+        # previous one drains (the 7B shard's 35 buckets of 25e6: 3.10 ms
+        # against 3.21 on one stream, measured in one process on MI355X).
+        # The integer norm sums make the order of the buckets' atomic adds
+        # irrelevant.
+        if bucket_streams not in (1, 2):
+            raise ValueError("bucket_streams is 1 or 2")
+        self.bucket_streams = bucket_streams if self.bucket is not None else 1
+        self._side = torch.cuda.Stream(device=dev) if self.bucket_streams == 2 else None
+        # the side stream's buckets get their own one-shot workspace: calls
+        # that share one must not run concurrently
+        self._side_ws = B.new_reduce_workspace(dev) if self._side is not None else None
         self.skipped = torch.zeros(1, dtype=torch.int32, device=dev)
         self._skip_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
         self._skip_event = None
@@ -134,24 +147,37 @@ class ShardStep:
         B.zero_norm_acc_clear(self.acc)
         if self.path == "fused":
             return
-        for lo, hi in self._ranges():
-            g = self.g[lo:hi] if self.path == "materialize" else None
-            oneshot = hi - lo > self.oneshot_min
-            if self.mx_grads:
-                codes = [c[lo:hi] for c, _ in replicas]
-                scales = [sc[lo // 32:hi // 32] for _, sc in replicas]
-                if oneshot:
-                    B.zero_shard_reduce_mx_ws(codes, scales, self.inv_scale, self.reduce_ws,
-                                              g_out=g, acc=self.acc)
-                else:
-                    B.zero_shard_reduce_mx(codes, scales, self.inv_scale, g_out=g, acc=self.acc)
-                continue
-            views = [r[lo:hi] for r in replicas]
+        if self._side is None:
+            for lo, hi in self._ranges():
+                self._reduce_range(replicas, lo, hi)
+            return
+        main = torch.cuda.current_stream(self.master.device)
+        self._side.wait_stream(main)
+        for i, (lo, hi) in enumerate(self._ranges()):
+            with torch.cuda.stream(self._side if i % 2 else main):
+                self._reduce_range(replicas, lo, hi, self._side_ws if i % 2 else self.reduce_ws)
+        main.wait_stream(self._side)
+
+    def _reduce_range(self, replicas, lo: int, hi: int, ws=None) -> None:
+        """One reduce launch over [lo, hi) on the current stream; ranges above
+        oneshot_min take the one-shot form with workspace `ws`."""
+        ws = self.reduce_ws if ws is None else ws
+        g = self.g[lo:hi] if self.path == "materialize" else None
+        oneshot = hi - lo > self.oneshot_min
+        if self.mx_grads:
+            codes = [c[lo:hi] for c, _ in replicas]
+            scales = [sc[lo // 32:hi // 32] for _, sc in replicas]
             if oneshot:
-                B.zero_shard_reduce_ws(views, self.inv_scale, self.reduce_ws, g_out=g,
-                                       acc=self.acc)
+                B.zero_shard_reduce_mx_ws(codes, scales, self.inv_scale, ws, g_out=g,
+                                          acc=self.acc)
             else:
-                B.zero_shard_reduce(views, self.inv_scale, g_out=g, acc=self.acc)
+                B.zero_shard_reduce_mx(codes, scales, self.inv_scale, g_out=g, acc=self.acc)
+            return
+        views = [r[lo:hi] for r in replicas]
+        if oneshot:
+            B.zero_shard_reduce_ws(views, self.inv_scale, ws, g_out=g, acc=self.acc)
+        else:
+            B.zero_shard_reduce(views, self.inv_scale, g_out=g, acc=self.acc)
 
     def _resolve_pending_skip(self) -> None:
         if self._skip_event is not None:
