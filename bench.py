@@ -53,6 +53,8 @@ def parse():
                     choices=["flat-1m-p4", "gpt2-small-p8", "1.3b-unsharded", "7b-shard-p8",
                              "30b-shard-p8", "30b-shard-p8-mxgrads"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="with the default 30B shard, skip the 7B shard's secondary timing")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements of the CPU-oracle sample")
     ap.add_argument("--cpu-steps", type=int, default=3)
@@ -200,7 +202,7 @@ def step_kernels(w):
     one-shot> (one-shot with P >= 4 above 2^27 elements a launch, where
     ShardStep passes the workspace, then a fold launch; else pipelined for
     P in {4, 8}), AdamW template <gradient source (-1: materialised g), P,
-    bf16 param, fused MXFP8>."""
+    bf16 param, fused MXFP8, tiles per workgroup>."""
     from zero_sharded_mixed_step_amd.step import ONESHOT_MIN
     path = _path_of(w)
     dt = 2 if w.mx_grads else (1 if w.grad_bf16 else 0)
@@ -211,6 +213,10 @@ def step_kernels(w):
     form = f"{pipe}, {'true' if oneshot else 'false'}"
     launches = -(-w.S // w.bucket) if w.bucket else 1
     mx = "true" if w.pack else "false"
+    # AdamW tiles per workgroup: 2, or 1 where two would give fewer than two
+    # workgroups per compute unit (256 on MI355X)
+    u = 1 if -(-(-(-(-(-w.S // 8)) // 256)) // 2) < 2 * 256 else 2
+    mx = f"{mx}, {u}"
     out = []
     fold = ("zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
             "adds the one-shot reduce's slots to the accumulator", launches)
@@ -561,7 +567,9 @@ def offload_bill(w, threads, sample, gpu_step_ms, reduce_ms):
     h2d_ms = 2 * S / (h2d * 1e9) * 1e3
     serial = reduce_ms + d2h_ms + cpu_ms + h2d_ms
     pipelined = reduce_ms + max(d2h_ms, cpu_ms, h2d_ms)
-    return {"d2h_gbps": round(d2h, 1), "h2d_gbps": round(h2d, 1),
+    return {"kind": "modelled: PCIe copy rates and the host AdamW rate measured on samples, "
+                    "scaled to the shard; no offloaded step runs end to end",
+            "d2h_gbps": round(d2h, 1), "h2d_gbps": round(h2d, 1),
             "cpu_adamw_params_per_s": round(cpu_rate, 1), "cpu_threads": threads,
             "per_step_ms": {"gpu_reduce": round(reduce_ms, 3), "d2h_g_f32": round(d2h_ms, 2),
                             "cpu_adamw": round(cpu_ms, 2), "h2d_param_bf16": round(h2d_ms, 2)},
@@ -585,6 +593,98 @@ def cpu_baseline_leg(w, args, threads, gpu_step_ms, reduce_ms):
     if not args.no_offload and reduce_ms is not None:
         res["offload_bill"] = offload_bill(w, threads, args.cpu_sample, gpu_step_ms, reduce_ms)
     return res
+
+
+def pattern_ceilings(w, st, reps, kinds, per_kernel):
+    """The bare access patterns of the step's two passes (libzs_patterns.so:
+    the same grids, access shapes and bytes, no arithmetic), on the step's
+    own buffers in this process, so the placement is the same: the ceiling
+    each kernel is measured against, next to the 8 TB/s peak.  Also the
+    bound of reading and writing serially at the read-only and write-only
+    rates.  Workloads whose step materialises fp32 g from 4 or 8 bf16
+    replicas (the 7B and 30B shards, the GPT-2-sized one); None otherwise.
+    The AdamW pattern writes master/m/v back unchanged; it overwrites only
+    outputs (g, param, MXFP8) that every step rewrites."""
+    import ctypes as C
+
+    import torch
+
+    from zero_sharded_mixed_step_amd import build as zb
+    if (w.mx_grads or not w.grad_bf16 or w.P not in (4, 8) or st.path != "materialize"
+            or not os.path.exists(zb.PATTERNS_LIB)):
+        return None
+    L = C.CDLL(zb.PATTERNS_LIB)
+    vp, sz = C.c_void_p, C.c_size_t
+    L.zs_pattern_read.argtypes = [vp, C.c_int, sz, vp, vp]
+    L.zs_pattern_write.argtypes = [vp, sz, vp]
+    L.zs_pattern_fill.argtypes = [vp, sz, vp]
+    L.zs_pattern_reduce.argtypes = [vp, C.c_int, sz, vp, vp]
+    L.zs_pattern_adamw.argtypes = [vp] * 7 + [sz, vp]
+    n = w.S // 2048 * 2048                       # whole tiles
+    ptrs = (vp * w.P)(*[r.data_ptr() for r in reps])
+    sink = torch.zeros(1 << 24, dtype=torch.int32, device=st.master.device)
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    mx = st.fuse_pack
+    elem = vp(st.mx_elem.data_ptr()) if mx else None
+    scale = vp(st.mx_scale.data_ptr()) if mx else None
+    g, ma, m, v, prm = (vp(t.data_ptr()) for t in (st.g, st.master, st.m, st.v, st.param))
+    runs = {
+        "read_only": (2 * w.P, lambda: L.zs_pattern_read(ptrs, w.P, n, vp(sink.data_ptr()),
+                                                         stream)),
+        "write_only": (4, lambda: L.zs_pattern_fill(g, n, stream)),
+        "write_g_store_shape": (4, lambda: L.zs_pattern_write(g, n, stream)),
+        "reduce_like": (2 * w.P + 4, lambda: L.zs_pattern_reduce(ptrs, w.P, n, g, stream)),
+        "adamw_like": (30 + (MX_BYTES if mx else 0),
+                       lambda: L.zs_pattern_adamw(g, ma, m, v, prm, elem, scale, n, stream)),
+    }
+    out = {}
+    for name, (bpe, fn) in runs.items():
+        if fn() != 0:
+            raise RuntimeError(f"pattern {name} did not launch")
+        evs = []
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+        out[name] = {"avg_ms": round(ms, 4), "bytes_per_elem": bpe,
+                     "gbps": round(bpe * n / (ms * 1e-3) / 1e9, 1)}
+    rd, wr = out["read_only"]["gbps"], out["write_only"]["gbps"]
+
+    def serial(r_bytes, w_bytes):
+        return round((r_bytes + w_bytes) / (r_bytes / rd + w_bytes / wr), 1)
+    res = {"note": "bare access patterns of the two passes on the step's own buffers, same "
+                   "grids, no arithmetic; median of 5 launches by HIP events.  read_only: the "
+                   "reduce's P nontemporal streams; write_only: the fastest write shape "
+                   "measured (plain 16-byte stores, 4 KB per workgroup); the serialised bound "
+                   "reads at read_only's and writes at write_only's rate",
+           "patterns": out,
+           "serialised_bound_gbps": {"reduce": serial(2 * w.P, 4),
+                                     "adamw": serial(16, 14 + (MX_BYTES if mx else 0))},
+           "kernel_frac_of_pattern": {}}
+    for k, pat in (("reduce", "reduce_like"), ("adamw", "adamw_like")):
+        if k in per_kernel:
+            res["kernel_frac_of_pattern"][k] = round(per_kernel[k]["gbps"] / out[pat]["gbps"], 4)
+    return res
+
+
+def context_fields(w):
+    """Closed forms the pages' figures rest on, beside the measured line:
+    state bytes per weight against weights alone, the 30B example's state per
+    data-parallel copy, and what MXFP8 saves on stored state and on the
+    wire."""
+    state = 2 + 2 + 4 + 4 + 4                     # bf16 param, bf16 grad, fp32 master, m, v
+    return {"state_bytes_per_weight": state, "weights_only_bytes_per_weight": 2,
+            "state_per_copy_gib_30b_model": round(30e9 * state / 2 ** 30, 2),
+            "copies_at_8_way_data_parallel": 8,
+            "mxfp8_bytes_per_elem": MX_BYTES,
+            "mxfp8_stored_state_saving": round(2 * (2 - MX_BYTES) / state, 4),
+            "mxfp8_wire_saving_vs_bf16": round(1 - MX_BYTES / 2, 4),
+            "this_shard_state_gb": round(w.S * state / 1e9, 2)}
 
 
 def workload_bytes(w):
@@ -671,48 +771,18 @@ def progress(msg):
     print(f"bench [{time.perf_counter() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: it runs one rank's shard step on a "
-              f"single MI355X, and the exchanges between ranks are not implemented "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
-
-    if args.summarize_pmc:
-        from synth import configs
-        summarize_pmc(configs.ALL[args.config], args.summarize_pmc, " ".join(sys.argv))
-        return
-    if args.trace_report:
-        from synth import configs
-        trace_report(configs.ALL[args.config], *args.trace_report)
-        return
-    if args.placement_report:
-        placement_report(args.placement_report)
-        return
-    if args.traffic_report:
-        traffic_report(args.traffic_report)
-        return
-
+def measure(w, args, dev, legs=True, recycle=True):
+    """One workload's timed steps and the figures around them; returns the
+    JSON object (without the CPU baseline) and what the CPU leg needs.
+    legs=False leaves out the unfused chain, the standalone pack, and the
+    cold and graph steps."""
     import torch
-
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
-    if args.placement_probe is not None:
-        from synth import configs
-        placement_probe(configs.ALL[args.config], args.placement_probe)
-        return
 
     import synth
     import zero_sharded_mixed_step_amd as zs
-    from synth import configs
 
-    w = configs.ALL[args.config]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    recycled = None if args.no_recycle else recycle_device_memory(dev, workload_bytes(w))
+    recycled = (None if args.no_recycle or not recycle
+                else recycle_device_memory(dev, workload_bytes(w)))
     grad_dtype = "mxfp8" if w.mx_grads else (torch.bfloat16 if w.grad_bf16 else torch.float32)
     st = zs.ShardStep(w.S, w.P, grad_dtype, lr=w.lr,
                       beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
@@ -791,7 +861,7 @@ def main():
     # The standalone MXFP8 pack entry point (outside the timed step: the step
     # packs inside AdamW), timed on its own for its roofline.
     standalone = {}
-    if w.pack:
+    if w.pack and legs:
         evs = []
         for _ in range(3):
             a = torch.cuda.Event(enable_timing=True)
@@ -806,7 +876,7 @@ def main():
                                     "gbps": round((2 + MX_BYTES) * w.S / (ms * 1e-3) / 1e9, 1)}
 
     unfused = None
-    if not args.no_unfused and not w.mx_grads:
+    if legs and not args.no_unfused and not w.mx_grads:
         # The same step as a chain of single-operation kernels, same process
         # and buffers: what fusion saves (bit-identical results).  The chain
         # takes the host step counter.
@@ -831,7 +901,7 @@ def main():
     # 256 MB MALL): a 1 GiB scratch write before each step evicts the state,
     # so the step reads it from HBM.  Timed by events around the step alone.
     cold = None
-    if sum(kinds.values()) * w.S < (2 << 30):
+    if legs and sum(kinds.values()) * w.S < (2 << 30):
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         n_warm = {k: len(v) for k, v in events.items()}
         cold_ev = []
@@ -857,7 +927,7 @@ def main():
     # The same small steps recorded once as a graph and replayed: what the
     # host's launches cost per step.  Timed by events around each replay.
     graph_steps = None
-    if sum(kinds.values()) * w.S < (2 << 30):
+    if legs and sum(kinds.values()) * w.S < (2 << 30):
         graph = st.capture(reps)
         graph.replay()
         torch.cuda.synchronize()
@@ -899,6 +969,18 @@ def main():
             per_launch = kinds[dom] * w.S if dom != "reduce" or not w.bucket else kinds[dom] * w.bucket
             traffic = (rec["kinds"][dom]["hbm_bytes"],
                        round(rec["kinds"][dom]["hbm_bytes"] / per_launch, 4))
+    patterns = pattern_ceilings(w, st, reps, kinds, per_kernel)
+    roof = {"bound": "hbm", "kernel": dom, "achieved": dom_gbps,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic[0] if traffic else None,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "scaled by a plain-copy calibration)",
+            "traffic_vs_algorithmic": traffic[1] if traffic else None}
+    if patterns and dom in patterns["kernel_frac_of_pattern"]:
+        pat = {"reduce": "reduce_like", "adamw": "adamw_like"}[dom]
+        roof["pattern_ceiling_gbps"] = patterns["patterns"][pat]["gbps"]
+        roof["frac_of_pattern"] = patterns["kernel_frac_of_pattern"][dom]
     out = {
         "metric": "optimizer-step params/sec per shard + achieved HBM GB/s (% of peak)",
         "value": round(params_per_s, 1),
@@ -931,21 +1013,75 @@ def main():
         "kernels": per_kernel,
         "standalone_kernels": standalone,
         "unfused_chain": unfused,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic[0] if traffic else None,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                     "scaled by a plain-copy calibration)",
-                     "traffic_vs_algorithmic": traffic[1] if traffic else None},
+        "roofline": roof,
+        "pattern_ceilings": patterns,
         "cpu_baseline": None,
+        "context": context_fields(w),
         "command": " ".join(["python", "bench.py", *sys.argv[1:]]),
     }
+    return out, {"ms_per_step": ms_per_step, "reduce_ms": kernel_ms.get("reduce"),
+                 "recycled": recycled}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: it runs one rank's shard step on a "
+              f"single MI355X, and the exchanges between ranks are not implemented "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    if args.summarize_pmc:
+        from synth import configs
+        summarize_pmc(configs.ALL[args.config], args.summarize_pmc, " ".join(sys.argv))
+        return
+    if args.trace_report:
+        from synth import configs
+        trace_report(configs.ALL[args.config], *args.trace_report)
+        return
+    if args.placement_report:
+        placement_report(args.placement_report)
+        return
+    if args.traffic_report:
+        traffic_report(args.traffic_report)
+        return
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    if args.placement_probe is not None:
+        from synth import configs
+        placement_probe(configs.ALL[args.config], args.placement_probe)
+        return
+
+    from synth import configs
+
+    w = configs.ALL[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out, ctx = measure(w, args, dev)
+    if args.config == "30b-shard-p8" and not args.no_secondary:
+        # The other shard the step is specified on, in the same process: the
+        # 7B rank share with its 35 buckets, its own timed steps.
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        sw = configs.SHARD_7B
+        sec, _ = measure(sw, args, dev, legs=False, recycle=False)
+        out["secondary"] = {k: sec[k] for k in (
+            "config", "value", "unit", "ms_per_step", "step_ms_median", "step_ms_p90",
+            "hbm_gbps", "hbm_frac", "bytes_per_param", "kernels", "roofline",
+            "pattern_ceilings")}
+        out["secondary"]["steps"] = args.steps
+        progress(f"secondary {sw.name}: {sec['ms_per_step']:.3f} ms/step")
     threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
     if not args.no_cpu_baseline:
         progress("CPU oracle baseline (bounded sample) starts")
-        out["cpu_baseline"] = cpu_baseline_leg(w, args, threads, ms_per_step,
-                                               kernel_ms.get("reduce"))
+        out["cpu_baseline"] = cpu_baseline_leg(w, args, threads, ctx["ms_per_step"],
+                                               ctx["reduce_ms"])
     print(json.dumps(out), flush=True)
 
 

@@ -23,15 +23,29 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+# The bare access patterns the benchmark measures as ceilings (not part of
+# the step's ABI; bench.py alone loads it).
+PATTERNS_LIB = os.path.join(HERE, "libzs_patterns.so")
+PATTERNS_SOURCES = [os.path.join(HERE, "csrc", "zs_patterns.hip")]
+
+
+def _compile(sources, out, defines, verbose):
     tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines],
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, *SOURCES]
+           "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, out: str = LIB, defines=(), patterns: bool = True) -> str:
+    """libzero_step.so (and, unless patterns=False, libzs_patterns.so)."""
+    _compile(SOURCES, out, defines, verbose)
+    if patterns:
+        _compile(PATTERNS_SOURCES, PATTERNS_LIB, (), verbose)
     return out
 
 

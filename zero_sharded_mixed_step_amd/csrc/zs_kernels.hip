@@ -491,10 +491,22 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamParams prm) {
     if (blockIdx.x == 0 && prm.skipped_out != nullptr) *prm.skipped_out = gt.skip;
   }
   __syncthreads();
-  const Gate gt = s_gate;
-  if (gt.skip) return;
-  const float coef = gt.coef;
-  const AdamScalars sc = s_sc;
+  // The gate and scalars are the same in every lane: read them into scalar
+  // registers (read from LDS they would each hold a VGPR per lane).
+  auto uniform = [](float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+  };
+  if (__builtin_amdgcn_readfirstlane(s_gate.skip)) return;
+  const float coef = uniform(s_gate.coef);
+  AdamScalars sc;
+  sc.b1 = uniform(s_sc.b1);
+  sc.b2 = uniform(s_sc.b2);
+  sc.omb1 = uniform(s_sc.omb1);
+  sc.omb2 = uniform(s_sc.omb2);
+  sc.step_size = uniform(s_sc.step_size);
+  sc.sqrt_bc2 = uniform(s_sc.sqrt_bc2);
+  sc.decay = uniform(s_sc.decay);
+  sc.eps = uniform(s_sc.eps);
   const float neg_step = -sc.step_size;
   // The update of one chunk from its loaded g and state; stores the new
   // state and param and leaves the param bits in pb (for the MXFP8 epilogue).
