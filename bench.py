@@ -838,9 +838,7 @@ def measure(w, args, dev, legs=True, recycle=True):
         step_events.append((sa, sb))
 
     def _launch_step():
-        if st.path == "fused":
-            zs.zero_norm_acc_clear(st.acc)
-        else:
+        if st.path != "fused":
             timed("reduce", lambda: st.reduce(reps))
         timed("adamw", lambda: st.update(reps))
         if w.pack and not st.fuse_pack:

@@ -143,10 +143,12 @@ class ShardStep:
                 yield lo, min(self.n, lo + self.bucket)
 
     def reduce(self, replicas: List[torch.Tensor]) -> None:
-        """Clear the accumulator and run the reduce/norm pass(es)."""
-        B.zero_norm_acc_clear(self.acc)
+        """Clear the accumulator and run the reduce/norm pass(es).  The fused
+        path (no gate) has none: its single pass reduces inside AdamW and
+        reads no accumulator."""
         if self.path == "fused":
             return
+        B.zero_norm_acc_clear(self.acc)
         if self._side is None:
             for lo, hi in self._ranges():
                 self._reduce_range(replicas, lo, hi)
@@ -283,6 +285,31 @@ class ShardStep:
             self._skip_event.record()
         else:
             self.t += 1
+
+    def state(self) -> dict:
+        """A checkpoint of the optimizer state: host copies of master, m, v and
+        the bf16 param, and the count of applied updates (waits for the work
+        queued so far).  The MXFP8 outputs are not state: every step rewrites
+        them from the param."""
+        t = self.applied_steps()
+        torch.cuda.synchronize(self.master.device)
+        return {"master": self.master.cpu(), "m": self.m.cpu(), "v": self.v.cpu(),
+                "param": self.param.cpu(), "t": t}
+
+    def load_state(self, state: dict) -> None:
+        """Restore a checkpoint taken by state() (same shard length): the
+        next step continues exactly where the saved run stood."""
+        for name in ("master", "m", "v", "param"):
+            src = state[name]
+            dst = getattr(self, name)
+            if src.numel() != dst.numel():
+                raise ValueError(f"{name}: checkpoint holds {src.numel()} elements, "
+                                 f"the shard {dst.numel()}")
+            dst.copy_(src.view(dst.dtype) if src.dtype != dst.dtype else src)
+        self._skip_event = None
+        self.t = int(state["t"])
+        if self.device_counter:
+            self.t_dev.fill_(self.t)
 
     def applied_steps(self) -> int:
         """Applied updates so far (waits for the last skip flag, or reads the
