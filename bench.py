@@ -3,14 +3,16 @@
 
 A step is one pass of the whole hot path over one batch of resident
 synthetic gradients: shard reduce of the P bf16 replicas with the average,
-overflow count and exact norm (bucketed where the workload says so), the
+non-finite count and exact norm (bucketed where the workload says so), the
 gated fused AdamW on fp32 master/m/v with the bf16 param write, and, for the
 30B workload, the MXFP8 pack of the param shard (the all-gather payload).
 
 Prints ONE JSON line: params/s of the shard (whole job = one GPU), HBM GB/s
 against the fused-minimum bytes, the roofline of the dominant kernel measured
-with HIP events inside the timed region, and the CPU oracle's rate on a
-bounded sample of the same workload.
+with HIP events inside the timed region, each kernel against the measured
+ceiling of its bare access pattern on the same buffers, and the CPU oracle's
+rate on a bounded sample of the same workload.  With the default 30B shard
+the 7B shard (35 buckets) is timed in the same process as "secondary".
 """
 import argparse
 import json
@@ -29,8 +31,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "include", "zero_step.h")] + [
     os.path.join(ROOT, "zero_sharded_mixed_step_amd", "csrc", f)
     for f in ("zs_abi.hip", "zs_device.h", "zs_internal.h", "zs_kernels.hip")]
 # kernel-name fragments of the launch kinds, as rocprofv3 reports them
-KERNEL_NAMES = {"reduce": "shard_reduce_kernel", "adamw": "adamw_kernel",
-                "mxfp8_pack": "mxfp8_kernel"}
+KERNEL_NAMES = {"reduce": "zs::shard_reduce_kernel", "adamw": "zs::adamw_kernel",
+                "mxfp8_pack": "zs::mxfp8_kernel"}   # the pattern kernels are not in zs::
 
 
 def source_digest() -> str:
@@ -273,6 +275,10 @@ def trace_report(w, prof_dir, bench_log):
     print("# shard_reduce_kernel / mxfp8_kernel launches of the chain); fill_kernel is the "
           "input generator and FillFunctor torch fills (set-up, untimed).")
     print(f"# Kernel sources digest (bench.py source_digest): {source_digest()}")
+    if w.bucket:
+        print("# Bucket reduces alternate over two streams and overlap: a launch lasts about "
+              "twice its share of the step (the bench line's kernels.reduce is the whole "
+              "bucketed pass, timed by events).")
     print("# Kernels of one step (role, launches per step, average ns from the table):")
     avg = {r["Name"]: float(r["AverageNs"]) for r in rows}
     for name, role, launches in step_kernels(w):

@@ -8,7 +8,7 @@ computes nothing itself.
 Pass structure (bytes per shard element; g_b = bytes per replica element):
   - no gate (no clip, no overflow check): one fused pass, AdamW reads the P
     replicas directly: P*g_b + 26 bytes;
-  - gated: the update waits for the global norm / overflow state, so either
+  - gated: the update waits for the global norm / non-finite count, so either
     materialise:  reduce writes fp32 g (+4) and AdamW re-reads it (+4), or
     recompute:    a norm-only pass over the replicas, then AdamW reduces the
                   replicas again (+P*g_b);
