@@ -153,7 +153,8 @@ int zero_shard_reduce_ws(const void *const *replicas, int P, int dtype, size_t n
  * as E4M3 codes plus one E8M0 scale per 32 elements, 1.03 instead of 2 bytes
  * per element).  Each element decodes exactly to
  *   x = e4m3_value(code) * 2^(scale - 127)   (binary32, exact; scale byte
- *   0xFF or a NaN code gives NaN),
+ *   0xFF or a NaN code gives the quiet NaN 0x7FC00000 with the code's sign
+ *   bit),
  * then g[i] = (x_0[i] + ... + x_{P-1}[i]) * inv_scale exactly as
  * zero_shard_reduce sums, with the same norm state.
  *   codes[k]   HOST array of P device pointers to uint8[n] E4M3 codes

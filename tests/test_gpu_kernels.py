@@ -187,13 +187,6 @@ def test_pipelined_reduce_many_iterations(zs, P, bf16):
 
 # ------------------------------------------------- MXFP8-stored replicas --
 
-def _same_or_both_nan(a: np.ndarray, b: np.ndarray) -> bool:
-    """Bitwise equal where finite or infinite; NaN exactly where the other is
-    NaN (the payload and sign of a NaN are not part of the result)."""
-    na, nb = np.isnan(a), np.isnan(b)
-    return a.shape == b.shape and np.array_equal(na, nb) and same_bits(a[~na], b[~nb])
-
-
 def test_mx_reduce_decodes_every_code_under_every_scale(zs):
     """P = 1, inv_scale = 1: the reduce output is the decoded MXFP8 value of
     all 256 codes under each of the 256 scale bytes (65536 pairs)."""
@@ -208,9 +201,9 @@ def test_mx_reduce_decodes_every_code_under_every_scale(zs):
     zs.zero_shard_reduce_mx([to_dev(codes)], [to_dev(scales)], 1.0, g_out=g, acc=acc)
     torch.cuda.synchronize()
     got = from_dev(g)
-    bad = np.nonzero(~((got == want) | (np.isnan(got) & np.isnan(want))))[0]
-    assert bad.size == 0, [(int(codes[i]), int(scales[i // 32]), got[i], want[i]) for i in bad[:6]]
-    assert _same_or_both_nan(got, want)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, [(int(codes[i]), int(scales[i // 32]), hex(got.view(np.uint32)[i]),
+                            hex(want.view(np.uint32)[i])) for i in bad[:6]]
     assert zs.read_norm_acc(acc)[0] == acc_from_oracle(O.norm_accumulate(want))
 
 
@@ -243,8 +236,8 @@ def test_mx_reduce_and_norm(zs, P):
         zs.zero_shard_reduce_mx_ws(codes, scales, inv, ws, g_out=g3, acc=acc3)
         torch.cuda.synchronize()
         got = from_dev(g)
-        assert _same_or_both_nan(got, want_g), mismatch_report(f"g n={n}", got, want_g)
-        assert _same_or_both_nan(from_dev(g3), want_g), n
+        assert same_bits(got, want_g), mismatch_report(f"g n={n}", got, want_g)
+        assert same_bits(from_dev(g3), want_g), n
         assert zs.read_norm_acc(acc)[0] == want_acc, n
         assert zs.read_norm_acc(acc2)[0] == want_acc, n
         assert zs.read_norm_acc(acc3)[0] == want_acc, n

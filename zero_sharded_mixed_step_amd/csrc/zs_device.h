@@ -31,11 +31,15 @@ struct Replicas {
 // Eight MXFP8 elements (codes in lo/hi, block scale byte sb) decoded to
 // binary32: v_cvt_pk_f32_fp8 gives the exact E4M3 value, and the product
 // with the power of two 2^(sb - 127) is exact too (at least 2^-136, at most
-// 448 * 2^127 before rounding of an overflow to inf); sb == 0xFF is NaN.
+// 448 * 2^127 before rounding of an overflow to inf).  A NaN code (0x7F or
+// 0xFF) or the NaN scale byte 0xFF gives the quiet NaN 0x7FC00000 with the
+// code's sign, written out explicitly so the bits do not depend on how the
+// conversion or the multiply propagates a NaN.
 __device__ __forceinline__ void decode_mx8(uint32_t lo, uint32_t hi, uint32_t sb,
                                            float x[8]) {
-  const float f = sb == 0xFFu ? __uint_as_float(0x7FC00000u)
-                  : (sb == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23));
+  // (scale byte 0xFF: any finite factor; those results are replaced below)
+  const float f = sb == 0u ? __uint_as_float(0x00400000u)
+                           : __uint_as_float((sb == 0xFFu ? 0x7Fu : sb) << 23);
   const uint32_t w[2] = {lo, hi};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -45,6 +49,12 @@ __device__ __forceinline__ void decode_mx8(uint32_t lo, uint32_t hi, uint32_t sb
     x[4 * h + 1] = a[1] * f;
     x[4 * h + 2] = b[0] * f;
     x[4 * h + 3] = b[1] * f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t c = (w[h] >> (8 * q)) & 0xFFu;
+      if (sb == 0xFFu || (c & 0x7Fu) == 0x7Fu)
+        x[4 * h + q] = __uint_as_float(((c & 0x80u) << 24) | 0x7FC00000u);
+    }
   }
 }
 
