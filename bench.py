@@ -319,7 +319,7 @@ def traffic_report(names):
         print(f"#   rocprofv3 --pmc $CTR --output-format csv -d "
               f"$R/{counter_dir(data[n]['command'], 0)}_$CTR -o run "
               f"-- python3 $R/bench.py --config {n} --steps 2 --warmup 1 --no-cpu-baseline "
-              "--no-unfused")
+              "--no-unfused --no-secondary")
     print("# Scaled (no GPU), the commands recorded in profiles/hbm_traffic.json:")
     for n in names:
         print("#   python " + data[n]["command"])

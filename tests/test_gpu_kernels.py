@@ -838,7 +838,7 @@ def test_device_counter_matches_host_counter(zs):
     assert host.applied_steps() == dev.applied_steps() == 100_000
 
 
-@pytest.mark.parametrize("case", ["buckets", "recompute", "fused", "oneshot"])
+@pytest.mark.parametrize("case", ["buckets", "recompute", "fused", "oneshot", "oneshot_buckets"])
 def test_graph_replay_matches_eager(zs, case):
     """One step recorded once and replayed: after every replay, with eager
     work and synchronisation between replays, the state is bitwise that of
@@ -846,12 +846,16 @@ def test_graph_replay_matches_eager(zs, case):
     gate and fused MXFP8 (materialised g, a skipped replay); one bf16 replica
     with a loss scale and the overflow check (recompute path, a skipped
     replay); 4 fp32 replicas, no gate (one fused pass); 8 bf16 replicas on
-    the one-shot reduce, whose workspace each replay leaves zero."""
+    the one-shot reduce, whose workspace each replay leaves zero; the same in
+    34 one-shot buckets alternating over the two streams, each stream with
+    its own workspace."""
     import torch
     n = 65536 + 96
     if case == "oneshot":
         # the one-shot reduce (workspace) at this size too
         P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, oneshot_min=0), 5
+    elif case == "oneshot_buckets":
+        P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, bucket=32 * 61, oneshot_min=0), 3
     elif case == "buckets":
         P, dt, kw, skip_call = 8, torch.bfloat16, dict(_HP, bucket=32 * 61), 4
     elif case == "recompute":
@@ -863,7 +867,10 @@ def test_graph_replay_matches_eager(zs, case):
     eager = zs.ShardStep(n, P, dt, device_counter=True, **kw)
     graphed = zs.ShardStep(n, P, dt, device_counter=True, **kw)
     assert eager.path == {"buckets": "materialize", "recompute": "recompute",
-                          "fused": "fused", "oneshot": "materialize"}[case]
+                          "fused": "fused", "oneshot": "materialize",
+                          "oneshot_buckets": "materialize"}[case]
+    if case in ("buckets", "oneshot_buckets"):
+        assert graphed._side is not None
     _init(eager, graphed)
     reps = [torch.empty(n, dtype=torch.int16 if dt == torch.bfloat16 else torch.float32,
                         device="cuda") for _ in range(P)]
@@ -889,6 +896,8 @@ def test_graph_replay_matches_eager(zs, case):
         assert _same_state(eager, graphed), call
         assert eager.applied_steps() == graphed.applied_steps()
         assert int(graphed.reduce_ws.abs().sum().item()) == 0, call
+        if graphed._side_ws is not None:
+            assert int(graphed._side_ws.abs().sum().item()) == 0, call
     assert graphed.applied_steps() == (6 if skip_call else 7)
 
 
