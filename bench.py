@@ -903,23 +903,23 @@ def measure(w, args, dev, legs=True, recycle=True):
 
     # Cold steps for workloads whose step fits in the caches (L2 4 MB per XCD,
     # 256 MB MALL): a 1 GiB scratch write before each step evicts the state,
-    # so the step reads it from HBM.  Timed by events around the step alone.
+    # so the step reads it from HBM.  Timed by two events around the step's
+    # launches alone (no per-kernel events inside, whose markers would add
+    # to a step of a few microseconds); the scratch write keeps the GPU busy
+    # while the host queues them.
     cold = None
     if legs and sum(kinds.values()) * w.S < (2 << 30):
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        n_warm = {k: len(v) for k, v in events.items()}
         cold_ev = []
         for _ in range(args.steps):
             scratch.fill_(1)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
-            _launch_step()
+            st.step(reps)
             b.record()
             cold_ev.append((a, b))
         torch.cuda.synchronize()
-        for k in events:                      # per-kernel figures stay warm-only
-            del events[k][n_warm[k]:]
         del scratch
         cold_ms = statistics.median(a.elapsed_time(b) for a, b in cold_ev)
         cold = {"step_ms_median": round(cold_ms, 4),
@@ -928,28 +928,28 @@ def measure(w, args, dev, legs=True, recycle=True):
                 "note": "1 GiB scratch write before each step (evicts L2 and MALL)"}
         st.applied_steps()
 
-    # The same small steps recorded once as a graph and replayed: what the
-    # host's launches cost per step.  Timed by events around each replay.
+    # The same small steps recorded once as a graph and replayed back to back:
+    # the steady-state rate of a loop that replays it (whichever of the
+    # GPU's work and the host's graph launches is slower sets it).
     graph_steps = None
     if legs and sum(kinds.values()) * w.S < (2 << 30):
         graph = st.capture(reps)
         graph.replay()
         torch.cuda.synchronize()
-        g_ev = []
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
         g0 = time.perf_counter()
+        a.record()
         for _ in range(args.steps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
             graph.replay()
-            b.record()
-            g_ev.append((a, b))
+        b.record()
         torch.cuda.synchronize()
         g_wall = 1e3 * (time.perf_counter() - g0) / args.steps
-        g_ms = statistics.median(a.elapsed_time(b) for a, b in g_ev)
-        graph_steps = {"step_ms_median": round(g_ms, 4), "wall_ms_per_step": round(g_wall, 4),
+        g_ms = a.elapsed_time(b) / args.steps
+        graph_steps = {"ms_per_step": round(g_ms, 4), "wall_ms_per_step": round(g_wall, 4),
                        "params_per_s": round(w.S / (g_wall * 1e-3), 1),
-                       "note": "one recorded step (all its launches) replayed per step"}
+                       "note": f"one recorded step (all its launches) replayed {args.steps} "
+                               "times back to back; ms_per_step by events around them all"}
         del graph
 
     ms_per_step = 1e3 * elapsed / args.steps
