@@ -414,6 +414,109 @@ def test_adamw_multi_step(zs, source, gated):
                 assert int(skipped.item()) == 0
 
 
+# IEEE corner values of the update: zeros of both signs, subnormals, the
+# edges of the normal range, values whose squares underflow or overflow,
+# infinities and NaN, in gradients and in the state.
+_CORNER_G = [0.0, -0.0, 1e-45, -1e-45, 1e-40, -3e-39, 1.1754942e-38, 1.17549435e-38, 1e-30,
+             -1e-20, 1e-3, -0.5, 1.0, 1e19, -3e19, 1e30, 3.4028235e38, -3.4028235e38,
+             np.inf, -np.inf, np.nan]
+_CORNER_MASTER = [0.0, -0.0, 1e-45, -1e-40, 1.17549435e-38, 0.02, -1.5, 1e30, 3.4028235e38,
+                  -np.inf]
+_CORNER_M = [0.0, -0.0, 1e-45, -1e-40, 1e-30, 1e-3, -0.2, 1e30, 3.4028235e38]
+_CORNER_V = [0.0, 1e-45, 1e-40, 1.17549435e-38, 1e-20, 1e-6, 1.0, 1e30, 3.4028235e38]
+# (lr, beta1, beta2, eps, weight_decay): the usual set, beta1 = 0 with eps = 0
+# (0/0 where v is zero), beta2 = 0 with full decay (lr * wd = 1)
+_CORNER_HP = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (0.1, 0.0, 0.5, 0.0, 0.0),
+              (1.0, 0.999, 0.0, 1e-30, 1.0)]
+
+
+def _same_or_nan(got, want, bf16=False):
+    """Bit for bit, except that where the oracle holds a NaN the device must
+    hold a NaN of any sign and payload: IEEE 754 leaves both open for the
+    result of an invalid operation (inf * 0, inf - inf, 0 / 0), and x86
+    returns the negative default NaN where the GPU returns the positive one."""
+    if bf16:
+        gb, wb = got.view(np.uint16), want.view(np.uint16)
+        gn, wn = (gb & 0x7FFF) > 0x7F80, (wb & 0x7FFF) > 0x7F80
+    else:
+        gb, wb = got.view(np.uint32), want.view(np.uint32)
+        gn, wn = np.isnan(got), np.isnan(want)
+    return got.shape == want.shape and np.array_equal(gn, wn) and np.array_equal(gb[~wn], wb[~wn])
+
+
+@pytest.mark.parametrize("source", ["grad_f32", "bf16_P3"])
+@pytest.mark.parametrize("gate", ["none", "clip_finite", "clip_nonfinite"])
+def test_adamw_ieee_corner_values(zs, source, gate):
+    """Three steps on corner-valued gradients and state, against the oracle:
+    subnormal inputs and products (no flush to zero), g^2 overflowing into an
+    infinite v, 0/0 with eps = 0, a clip coefficient that rounds to a
+    subnormal (huge finite gradients), coef = 0 on non-finite gradients
+    (inf * 0 = NaN).  The bf16 source also reduces corner-valued replicas,
+    its fp32 g and norm state compared where the step materialises them."""
+    import torch
+    n = 4 * 2048 + 37
+    rng = np.random.default_rng(7)
+    gvals = np.array([x for x in _CORNER_G if gate != "clip_finite" or np.isfinite(x)],
+                     np.float32)
+    P, bf16 = (1, False) if source == "grad_f32" else (3, True)
+    if bf16 and gate == "clip_finite":
+        # the largest binary32 rounds to inf in bf16, and a sum of three
+        # bf16 maxima overflows binary32
+        gvals = gvals[np.abs(gvals) < 1e37]
+    reached_subnormal = reached_nan = False
+    for hp in _CORNER_HP:
+        master = rng.choice(np.array(_CORNER_MASTER, np.float32), n)
+        m = rng.choice(np.array(_CORNER_M, np.float32), n)
+        v = rng.choice(np.array(_CORNER_V, np.float32), n)
+        param = O.f32_to_bf16(master)
+        d = [to_dev(a) for a in (master, m, v, param)]
+        acc = zs.new_norm_acc(1)
+        g_dev = torch.empty(n, dtype=torch.float32, device="cuda")
+        max_norm = 0.0 if gate == "none" else 1.0
+        for t in range(1, 4):
+            reps = [rng.choice(gvals, n) for _ in range(P)]
+            if gate == "clip_nonfinite":
+                reps[0][rng.integers(0, n)] = np.inf
+            if bf16:
+                reps = [O.f32_to_bf16(r) for r in reps]
+            inv = O.inv_scale(P, 1.0)
+            g = O.reduce(reps, inv)
+            want_acc = O.norm_accumulate(g)
+            skip, coef = O.gate(want_acc, max_norm, False)
+            assert not skip
+            if gate == "clip_finite":
+                assert 0.0 < coef < 1.0
+            if gate == "clip_nonfinite":
+                assert coef == 0.0
+            O.adamw(g, coef, O.make_scalars(*hp, t), master, m, v, param)
+            dreps = [to_dev(r) for r in reps]
+            kw = dict(step=t, lr=hp[0], beta1=hp[1], beta2=hp[2], eps=hp[3], weight_decay=hp[4],
+                      param_bf16=d[3])
+            if gate != "none":
+                zs.zero_norm_acc_clear(acc)
+                zs.zero_shard_reduce(dreps, inv, g_out=g_dev, acc=acc)
+                kw.update(accs=acc, max_norm=max_norm, check_overflow=False)
+                zs.zero_adamw_step(d[0], d[1], d[2], grad_f32=g_dev, **kw)
+                torch.cuda.synchronize()
+                assert _same_or_nan(from_dev(g_dev), g), f"g, step {t}, hp {hp}"
+                assert zs.read_norm_acc(acc)[0] == (want_acc.X, int(want_acc.nonfinite)), t
+            elif source == "grad_f32":
+                zs.zero_adamw_step(d[0], d[1], d[2], grad_f32=to_dev(g), **kw)
+            else:
+                zs.zero_adamw_step(d[0], d[1], d[2], replicas=dreps, inv_scale=inv, **kw)
+            torch.cuda.synchronize()
+            for name, got, want in zip(("master", "m", "v", "param"), d, (master, m, v, param)):
+                hg = from_dev(got, name == "param")
+                assert _same_or_nan(hg, want, name == "param"), \
+                    mismatch_report(f"{name} step {t} hp {hp}", hg, want)
+            sub = [a[(a != 0) & (np.abs(a) < 1.17549435e-38)] for a in (master, m, v)]
+            reached_subnormal |= any(x.size for x in sub)
+            reached_nan |= bool(np.isnan(master).any())
+    # the corners were reached: subnormal state, and NaN where g holds a non-finite
+    assert reached_subnormal
+    assert reached_nan or gate == "clip_finite"
+
+
 def test_adamw_fused_mxfp8_epilogue(zs):
     import torch
     for n, P, bf16 in ((32, 1, True), (4096 + 32, 8, True), (32 * 30011, 4, False)):
