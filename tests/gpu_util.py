@@ -87,9 +87,18 @@ def oracle_norm_parallel(workload, call, lo, hi, threads=THREADS):
     return total
 
 
+CAPTURE = None     # pytest's capture manager, set by conftest
+
+
 def log(msg):
-    """Progress line of a long parity test (shown with pytest -s)."""
-    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    """Progress line of a long parity test, written to the terminal at once
+    even while pytest captures the test's output."""
+    line = f"[parity {time.strftime('%H:%M:%S')}] {msg}"
+    if CAPTURE is None:
+        print(line, flush=True)
+        return
+    with CAPTURE.global_and_fixture_disabled():
+        print(line, flush=True)
 
 
 def _chunks(n, chunk):

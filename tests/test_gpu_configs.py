@@ -19,9 +19,8 @@ from the counter-based generator (OracleRun).
     skipped), 7B shard (10 steps, 35 buckets of 25M, clip), 30B shard (5
     steps, clip + overflow check, MXFP8 pack fused, then the standalone
     pack): whole schedules, every element.
-  - 30B shard with MXFP8-stored gradient replicas: the host packs and
-    decodes all 8 replicas of every chunk at every call, which is what
-    bounds its length (the first two of its five calls).
+  - 30B shard with MXFP8-stored gradient replicas, all five calls: the host
+    packs and decodes all 8 replicas of every chunk at every call.
 """
 import numpy as np
 import pytest
@@ -244,9 +243,9 @@ def test_30b_shard_clip_overflow_then_mxfp8(zs):
 
 @pytest.mark.timeout(1200)
 def test_30b_shard_mxfp8_stored_grads(zs):
-    # the first two of the five calls: the host packs and decodes every
-    # replica chunk of every call (8 x 3.75e9 elements per call)
+    # all five calls; the host packs and decodes every replica chunk of every
+    # call (8 x 3.75e9 elements per call, about 80 s on 16 threads)
     w = configs.SHARD_30B_MX
-    st, run = _run_full(zs, w, calls=range(1, 3))
-    assert st.path == "materialize" and run.t == 2
+    st, run = _run_full(zs, w, calls=range(1, w.steps + 1), pack_checks=True)
+    assert st.path == "materialize" and run.t == w.steps
     del st
