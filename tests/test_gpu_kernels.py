@@ -602,8 +602,8 @@ def test_gated_step_past_2_32_elements(zs):
     """64-bit indexing and one norm call over more than 2^32 elements: a
     gated step (clip 1.0 and the overflow check) of one bf16 replica on
     n > 2^32 elements (about 73 GB of state), with the MXFP8 pack fused.  One
-    gradient of 2^34 (a group norm of about 1.7e10, past the old 2^32 group
-    limit) dominates the norm, so the clip coefficient depends on it.  The
+    gradient of 2^34 (a group norm of about 1.7e10, a group sum of squares
+    past 2^64) dominates the norm, so the clip coefficient depends on it.  The
     oracle computes the global norm over all n elements on the host, then
     follows sampled blocks around the 2^31 and 2^32 element boundaries, the
     large gradient and the ragged end."""
