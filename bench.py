@@ -367,6 +367,7 @@ def placement_report(pairs):
           "with TMPDIR=/tmp, repo at $R); each pass below gives its command.")
     print("# This summary: python bench.py --placement-report " + " ".join(
         f"{os.path.normpath(d)} {os.path.normpath(lg)}" for d, lg in runs))
+    print(f"# Kernel sources digest (bench.py source_digest): {source_digest()}")
     print("# Launch durations (ms) are rocprofv3's per-dispatch timestamps under counter "
           "collection.  TCC_EA0 DRAM read requests are 128 B, write requests 64 B; GMI = "
           "inter-die.")
@@ -1022,6 +1023,7 @@ def measure(w, args, dev, legs=True, recycle=True):
         "cpu_baseline": None,
         "context": context_fields(w),
         "command": " ".join(["python", "bench.py", *sys.argv[1:]]),
+        "kernel_sources_digest": source_digest(),
     }
     return out, {"ms_per_step": ms_per_step, "reduce_ms": kernel_ms.get("reduce"),
                  "recycled": recycled}
