@@ -66,7 +66,11 @@ def parse():
                     help="threads of the all-cores oracle legs (capped by the host)")
     ap.add_argument("--no-recycle", action="store_true",
                     help="allocate the workload without first writing and releasing a "
-                         "scratch allocation of its size")
+                         "scratch allocation of its size (same as --memory-prep none)")
+    ap.add_argument("--memory-prep", choices=("recycle", "spacer", "none"), default="recycle",
+                    help="untimed set-up before the workload allocates: write and release "
+                         "a scratch allocation (recycle), write and hold a 60 GB spacer "
+                         "for the whole run (spacer), or nothing")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused single-operation chain")
     ap.add_argument("--trace-report", nargs=2, metavar=("PROF_DIR", "BENCH_LOG"),
@@ -724,6 +728,23 @@ def recycle_device_memory(dev, nbytes):
     return size
 
 
+_HELD = []
+
+
+def hold_spacer(dev, nbytes):
+    """Untimed set-up: allocate, write and hold (until the process ends) a
+    spacer of nbytes in 5 GB pieces before the workload allocates.  Returns
+    the bytes held."""
+    import torch
+    while sum(x.numel() for x in _HELD) < nbytes:
+        x = torch.empty(min(5 * 10**9, nbytes - sum(y.numel() for y in _HELD)),
+                        dtype=torch.uint8, device=dev)
+        x.fill_(1)
+        _HELD.append(x)
+    torch.cuda.synchronize(dev)
+    return sum(x.numel() for x in _HELD)
+
+
 def placement_probe(w, spacer_gb):
     """Time the step's reduce and AdamW launches with the workload's buffers
     allocated first in the process, then again after a held, written spacer
@@ -788,8 +809,15 @@ def measure(w, args, dev, legs=True, recycle=True):
     import synth
     import zero_sharded_mixed_step_amd as zs
 
-    recycled = (None if args.no_recycle or not recycle
-                else recycle_device_memory(dev, workload_bytes(w)))
+    prep = "none" if args.no_recycle or not recycle else args.memory_prep
+    if prep == "recycle":
+        recycled = recycle_device_memory(dev, workload_bytes(w))
+        prep_note = f"{recycled} B scratch written and released before allocating"
+    elif prep == "spacer":
+        recycled = hold_spacer(dev, 60 * 10**9)
+        prep_note = f"{recycled} B spacer written and held for the whole run"
+    else:
+        recycled, prep_note = None, "none"
     grad_dtype = "mxfp8" if w.mx_grads else (torch.bfloat16 if w.grad_bf16 else torch.float32)
     st = zs.ShardStep(w.S, w.P, grad_dtype, lr=w.lr,
                       beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
@@ -1009,8 +1037,7 @@ def measure(w, args, dev, legs=True, recycle=True):
                    "max_norm": w.max_norm, "check_overflow": w.check_overflow,
                    "mxfp8_pack": ("fused into AdamW" if st.fuse_pack else "separate pass")
                    if w.pack else False, "path": st.path},
-        "memory_prep": (f"{recycled} B scratch written and released before allocating"
-                        if recycled else "none"),
+        "memory_prep": prep_note,
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_param": sum(kinds.values()),
