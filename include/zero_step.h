@@ -34,9 +34,12 @@
  *     default stream) and is asynchronous: a return of ZERO_OK means the
  *     kernels were launched.  Faults inside them surface at the caller's next
  *     synchronisation.
+ *   - Every device pointer is memory of the current HIP device, on which the
+ *     kernels are launched (`stream` must belong to it too).
  *   - The caller owns every buffer.  The library allocates nothing, never
- *     synchronises, keeps no state between calls, and lets no C++ exception
- *     escape.
+ *     synchronises, and lets no C++ exception escape.  It keeps no state
+ *     between calls, except zero_shard_reduce_noalloc's static per-device
+ *     slots (described there).
  *   - Alignment (ZERO_EALIGN otherwise): every device array and every
  *     zero_norm_acc must be 16-byte aligned; the exceptions are the
  *     per-block scale bytes of MXFP8-stored replicas (any alignment), the

@@ -98,6 +98,9 @@ def _dev_ptr(t, name):
         return None
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the library launches on the current "
+                         f"device, cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return C.c_void_p(t.data_ptr())
@@ -364,6 +367,9 @@ def zero_adamw_step_unfused(master, m, v, workspace, *, step, lr, beta1=0.9, bet
     """The step as a chain of single-operation kernels (`accs`: the OTHER
     ranks' accumulators; `workspace`: a uint8 device tensor of at least
     zero_unfused_workspace_bytes(n, k) bytes)."""
+    if workspace is None:
+        raise ValueError("the unfused chain needs a workspace of "
+                         "zero_unfused_workspace_bytes(n, k) bytes")
     a, keep = _adam_args(master, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_f32,
                          replicas, inv_scale, param_bf16, accs, max_norm, check_overflow,
                          skipped_out, mx_elem_out, mx_scale_out, n)
