@@ -1,7 +1,10 @@
 // zs_kernels.hip -- the optimizer step's HIP kernels for CDNA4 (gfx950).
 //
-// All four are HBM-bandwidth-bound streaming passes (no matrix work, so no
-// MFMA): 16-byte vector loads/stores per lane over 2048-element tiles.
+// The three streaming passes -- the shard reduce, AdamW and the MXFP8 pack --
+// are HBM-bandwidth-bound (no matrix work, so no MFMA): 16-byte vector
+// loads/stores per lane over 2048-element tiles.  Small one-workgroup
+// kernels fold the reduce's slots, evaluate the gate, advance the device
+// step counter and clear accumulators.
 // AdamW, the pack and (given a workspace) the reduce of 4 or more replicas
 // run one-shot grids of a few tiles per workgroup; the reduce's norm state
 // (reduced in registers by quad DPP, then in lane-private LDS rows) then
