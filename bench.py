@@ -514,6 +514,121 @@ def cpu_baseline(w, sample, steps, threads=1):
             "host_cpus": os.cpu_count()}
 
 
+def offloaded_step_measured(w, threads, sample, gpu_step_ms, chunks=8, steps=3):
+    """The offloaded step run end to end on the first `sample` elements of
+    the shard: the GPU reduces bf16 replicas (the library's reduce, with the
+    norm state); the fp32 gradient and the 128-byte norm state cross PCIe to
+    pinned host memory; the host evaluates the gate and runs AdamW on all
+    its cores over the host-resident master/m/v (the oracle's gate and
+    AdamW, threaded over slices); the bf16 param crosses back.  Serial: one
+    phase after the other.  Pipelined: the gradient crosses in `chunks`
+    pieces on one stream while the host updates the pieces that have
+    landed, and each updated piece's param crosses back on another stream.
+    Each figure is the median of `steps` steps after one untimed step,
+    scaled to the shard by S / sample."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    import synth
+    import zero_sharded_mixed_step_amd as zs
+    from concurrent.futures import ThreadPoolExecutor
+    dev = torch.device("cuda:0")
+    n = min(sample, w.S) // 32 * 32
+    start = w.shard_start()
+    reps = []
+    for k in range(w.P):
+        r = torch.empty(n, dtype=torch.int16, device=dev)
+        synth.fill_device(w.grad_spec(1, k), start, r)
+        reps.append(r)
+    g_dev = torch.empty(n, dtype=torch.float32, device=dev)
+    p_dev = torch.empty(n, dtype=torch.int16, device=dev)
+    acc = zs.new_norm_acc(1, dev)
+    g_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
+    p_host = torch.zeros(n, dtype=torch.int16, pin_memory=True)
+    acc_host = torch.empty((1, zs.ACC_WORDS), dtype=torch.int64, pin_memory=True)
+    g_np, p_np = g_host.numpy(), p_host.numpy().view(np.uint16)
+    master = synth.fill(w.master_spec(), start, n, False, threads=8)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    inv = zs.zero_inv_scale(w.P, w.loss_scale)
+    d2h_s, h2d_s = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    pieces = O._cuts(n, chunks)
+    torch.cuda.synchronize()
+
+    def host_gate():
+        X, nonfinite = zs.read_norm_acc(acc_host)[0]
+        a = O.acc_zero()
+        for k in range(O.ACC_WORDS):
+            a.w[k] = (X >> (32 * k)) & 0xFFFFFFFF
+        a.nonfinite = nonfinite
+        return O.gate(a, w.max_norm, w.check_overflow)
+
+    def host_adamw(ex, lo, hi, coef, sc):
+        cuts = [(lo + a, lo + b) for a, b in O._cuts(hi - lo, threads)]
+        list(ex.map(lambda c: O.adamw(g_np[c[0]:c[1]], coef, sc, master[c[0]:c[1]],
+                                      m[c[0]:c[1]], v[c[0]:c[1]], p_np[c[0]:c[1]]), cuts))
+
+    def gpu_reduce():
+        zs.zero_norm_acc_clear(acc)
+        zs.zero_shard_reduce(reps, inv, g_out=g_dev, acc=acc)
+
+    def serial_step(ex, t):
+        gpu_reduce()
+        g_host.copy_(g_dev, non_blocking=True)
+        acc_host.copy_(acc, non_blocking=True)
+        torch.cuda.synchronize()
+        skip, coef = host_gate()
+        if not skip:
+            host_adamw(ex, 0, n, coef, O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, t))
+        p_dev.copy_(p_host, non_blocking=True)
+        torch.cuda.synchronize()
+
+    def pipelined_step(ex, t):
+        gpu_reduce()
+        acc_host.copy_(acc, non_blocking=True)
+        reduced = torch.cuda.Event()
+        reduced.record()
+        d2h_s.wait_event(reduced)
+        landed = []
+        with torch.cuda.stream(d2h_s):
+            for a, b in pieces:
+                g_host[a:b].copy_(g_dev[a:b], non_blocking=True)
+                e = torch.cuda.Event()
+                e.record(d2h_s)
+                landed.append(e)
+        reduced.synchronize()
+        skip, coef = host_gate()
+        sc = O.make_scalars(w.lr, w.beta1, w.beta2, w.eps, w.wd, t)
+        for (a, b), e in zip(pieces, landed):
+            e.synchronize()
+            if not skip:
+                host_adamw(ex, a, b, coef, sc)
+            with torch.cuda.stream(h2d_s):
+                p_dev[a:b].copy_(p_host[a:b], non_blocking=True)
+        h2d_s.synchronize()
+
+    times = {"serial": [], "pipelined": []}
+    t = 0
+    with ThreadPoolExecutor(threads) as ex:
+        for name, fn in (("serial", serial_step), ("pipelined", pipelined_step)):
+            for i in range(steps + 1):
+                t += 1
+                t0 = time.perf_counter()
+                fn(ex, t)
+                if i:                                   # the first is untimed
+                    times[name].append(1e3 * (time.perf_counter() - t0))
+    scale = w.S / n
+    serial = statistics.median(times["serial"]) * scale
+    pipelined = statistics.median(times["pipelined"]) * scale
+    return {"sample_elems": n, "chunks": chunks, "cpu_threads": threads,
+            "sample_ms_per_step": {k: round(statistics.median(v_), 3)
+                                   for k, v_ in times.items()},
+            "offloaded_ms_per_step_serial": round(serial, 2),
+            "offloaded_ms_per_step_pipelined": round(pipelined, 2),
+            "slowdown_serial": round(serial / gpu_step_ms, 1),
+            "slowdown_pipelined": round(pipelined / gpu_step_ms, 1)}
+
+
 def offload_bill(w, threads, sample, gpu_step_ms, reduce_ms):
     """What the step costs with the optimizer moved to the host (the
     offloading the ZeRO pages describe): the GPU still reduces (its measured
@@ -578,20 +693,27 @@ def offload_bill(w, threads, sample, gpu_step_ms, reduce_ms):
     h2d_ms = 2 * S / (h2d * 1e9) * 1e3
     serial = reduce_ms + d2h_ms + cpu_ms + h2d_ms
     pipelined = reduce_ms + max(d2h_ms, cpu_ms, h2d_ms)
-    return {"kind": "modelled: PCIe copy rates and the host AdamW rate measured on samples, "
-                    "scaled to the shard; no offloaded step runs end to end",
-            "d2h_gbps": round(d2h, 1), "h2d_gbps": round(h2d, 1),
-            "cpu_adamw_params_per_s": round(cpu_rate, 1), "cpu_threads": threads,
-            "per_step_ms": {"gpu_reduce": round(reduce_ms, 3), "d2h_g_f32": round(d2h_ms, 2),
-                            "cpu_adamw": round(cpu_ms, 2), "h2d_param_bf16": round(h2d_ms, 2)},
-            "offloaded_ms_per_step_serial": round(serial, 2),
-            "offloaded_ms_per_step_pipelined": round(pipelined, 2),
+    measured = offloaded_step_measured(w, threads, sample, gpu_step_ms)
+    return {"kind": "measured: the offloaded step run end to end (GPU reduce, PCIe both ways, "
+                    "host gate and AdamW on all cores) on the first elements of the shard, "
+                    "serial and pipelined, scaled to the shard; beside it, the same bill "
+                    "composed from separately measured PCIe and host AdamW rates",
             "gpu_ms_per_step": round(gpu_step_ms, 3),
-            "slowdown_serial": round(serial / gpu_step_ms, 1),
-            "slowdown_pipelined": round(pipelined / gpu_step_ms, 1),
-            "sample": f"PCIe: 1 GiB D2H fp32 and 512 MiB H2D bf16, pinned, x3; CPU: oracle "
-                      f"AdamW on the first {sample} elements of the {w.name} shard x{reps_t}; "
-                      f"scaled to S={S}"}
+            "measured_end_to_end": measured,
+            "modelled": {
+                "d2h_gbps": round(d2h, 1), "h2d_gbps": round(h2d, 1),
+                "cpu_adamw_params_per_s": round(cpu_rate, 1), "cpu_threads": threads,
+                "per_step_ms": {"gpu_reduce": round(reduce_ms, 3),
+                                "d2h_g_f32": round(d2h_ms, 2), "cpu_adamw": round(cpu_ms, 2),
+                                "h2d_param_bf16": round(h2d_ms, 2)},
+                "offloaded_ms_per_step_serial": round(serial, 2),
+                "offloaded_ms_per_step_pipelined": round(pipelined, 2),
+                "slowdown_serial": round(serial / gpu_step_ms, 1),
+                "slowdown_pipelined": round(pipelined / gpu_step_ms, 1)},
+            "sample": f"end to end: the first {measured['sample_elems']} elements of the "
+                      f"{w.name} shard, {measured['chunks']} pieces when pipelined; modelled: "
+                      f"1 GiB D2H fp32 and 512 MiB H2D bf16, pinned, x3, and the oracle's "
+                      f"AdamW on the first {sample} elements x{reps_t}; scaled to S={S}"}
 
 
 def cpu_baseline_leg(w, args, threads, gpu_step_ms, reduce_ms):

@@ -6,7 +6,8 @@ names as the C entry points) plus `ShardStep`, which sequences the calls of
 one step.  There is no host fallback: loading fails if the library is not
 built.
 """
-from ._binding import (REDUCE_WORKSPACE_BYTES, ZERO_BF16, ZERO_F32,  # noqa: F401
+from ._binding import (ACC_DIGITS, ACC_WORDS, REDUCE_WORKSPACE_BYTES, ZERO_BF16,  # noqa: F401
+                       ZERO_F32,
                        ZERO_MAX_REPLICAS, ZERO_MXFP8, ZeroStepError, lib, new_norm_acc,
                        new_reduce_workspace, read_norm_acc, zero_abi_version, zero_adamw_step,
                        zero_adamw_step_unfused, zero_grad_norm, zero_inv_scale, zero_mxfp8_pack,
