@@ -12,7 +12,8 @@ or none, the one-shot or pipelined reduce, a forced pass structure, the
 fused or standalone pack, the host or device step counter, one or two
 bucket streams, and the AdamW hyperparameters.  With the overflow check on,
 some cases put an infinity into one replica at one call, which the gate
-must skip.
+must skip.  Forty more configurations run as a recorded graph, replayed for
+each call on fresh gradients and compared after every replay.
 """
 import numpy as np
 import pytest
@@ -137,3 +138,86 @@ def test_random_step_configuration(zs, case):
         want_e, want_s = O.mxfp8_pack(param)
         assert same_bits(from_dev(st.mx_elem), want_e), f"{where} mxfp8 codes"
         assert same_bits(from_dev(st.mx_scale), want_s), f"{where} mxfp8 scales"
+
+
+N_GRAPH_CASES = 40
+
+
+@pytest.mark.parametrize("case", range(N_GRAPH_CASES))
+def test_random_configuration_graph_replay(zs, case):
+    """A random configuration (as above, with the device step counter that
+    recording needs) recorded once as a graph and replayed for three calls,
+    with fresh gradients written into the same replica buffers by eager
+    work between the replays: after every replay the state is bit for bit
+    the oracle's."""
+    import torch
+    c = _draw(10_000 + case)
+    c["device_counter"] = True
+    n, P, kind = c["n"], c["P"], c["kind"]
+    gdt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": "mxfp8"}[kind]
+    st = zs.ShardStep(n, P, gdt, lr=c["lr"], beta1=c["beta1"], beta2=c["beta2"], eps=c["eps"],
+                      weight_decay=c["weight_decay"], max_norm=c["max_norm"],
+                      check_overflow=c["check_overflow"], loss_scale=c["loss_scale"],
+                      bucket=c["bucket"], pack=c["pack"], fuse_pack=c["fuse_pack"],
+                      path=c["path"], device_counter=True, oneshot_min=c["oneshot_min"],
+                      bucket_streams=c["bucket_streams"])
+    mspec = synth.make_spec(seed=case, cfg=71, stream=0, sigma=0.02)
+    synth.fill_device(mspec, 0, st.master)
+    synth.fill_device(mspec, 0, st.param)
+    if c["pack"]:
+        st.mx_elem.zero_()
+        st.mx_scale.zero_()
+    master = synth.fill(mspec, 0, n, False)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    param = O.f32_to_bf16(master)
+    bf16_src = kind != "f32"
+    dev_src = [torch.empty(n, dtype=torch.int16 if bf16_src else torch.float32, device="cuda")
+               for _ in range(P)]
+    if kind == "mxfp8":
+        dev_reps = [(torch.empty(n, dtype=torch.uint8, device="cuda"),
+                     torch.empty(n // 32, dtype=torch.uint8, device="cuda")) for _ in range(P)]
+    else:
+        dev_reps = dev_src
+    inv = O.inv_scale(P, c["loss_scale"])
+
+    def fill(call):
+        host = [synth.fill(_grad_spec(10_000 + case, call, k, c["loss_scale"]), 0, n, bf16_src)
+                for k in range(P)]
+        for k, r in enumerate(dev_src):
+            synth.fill_device(_grad_spec(10_000 + case, call, k, c["loss_scale"]), 0, r)
+        if c["inject"] == call:
+            k, i = c["inject_at"]
+            host[k][i] = 0x7F80 if bf16_src else np.float32(np.inf)
+            dev_src[k][i] = 0x7F80 if bf16_src else float("inf")
+        if kind == "mxfp8":
+            for r, (codes, scales) in zip(dev_src, dev_reps):
+                zs.zero_mxfp8_pack(r, codes, scales)
+            host = [O.mxfp8_decode(*O.mxfp8_pack(r)) for r in host]
+        return host
+
+    torch.cuda.synchronize()
+    graph = st.capture(dev_reps)                 # records; runs nothing
+    torch.cuda.synchronize()
+    applied = 0
+    where = f"graph case {case} {c}"
+    for call in range(1, STEPS + 1):
+        host = fill(call)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        skipped, own = O.step(host, inv, c["max_norm"], c["check_overflow"], c["lr"],
+                              c["beta1"], c["beta2"], c["eps"], c["weight_decay"], applied + 1,
+                              master, m, v, param)
+        applied += 0 if skipped else 1
+        assert st.applied_steps() == applied, f"{where} call {call}"
+        for name, want in (("master", master), ("m", m), ("v", v), ("param", param)):
+            got = from_dev(getattr(st, name), name == "param")
+            assert same_bits(got, want), mismatch_report(f"{where} call {call} {name}", got, want)
+        if st.path != "fused":
+            assert zs.read_norm_acc(st.acc)[0] == acc_from_oracle(own), f"{where} call {call}"
+        if c["pack"] and applied:
+            want_e, want_s = O.mxfp8_pack(param)
+            assert same_bits(from_dev(st.mx_elem), want_e), f"{where} call {call} codes"
+            assert same_bits(from_dev(st.mx_scale), want_s), f"{where} call {call} scales"
+    del graph
