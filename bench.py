@@ -770,22 +770,35 @@ def pattern_ceilings(w, st, reps, kinds, per_kernel):
         "adamw_like": (30 + (MX_BYTES if mx else 0),
                        lambda: L.zs_pattern_adamw(g, ma, m, v, prm, elem, scale, n, stream)),
     }
-    out = {}
-    for name, (bpe, fn) in runs.items():
-        if fn() != 0:
-            raise RuntimeError(f"pattern {name} did not launch")
-        evs = []
-        for _ in range(5):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        ms = statistics.median(a.elapsed_time(b) for a, b in evs)
-        out[name] = {"avg_ms": round(ms, 4), "bytes_per_elem": bpe,
-                     "gbps": round(bpe * n / (ms * 1e-3) / 1e9, 1)}
+    # PyTorch's own elementwise kernels on the same buffers, as reference
+    # points for mixed reads and writes that this library did not write
+    # (they overwrite only g, which every step rewrites)
+    gv, mv, vv = st.g[:n], st.m[:n], st.v[:n]
+    vendor_runs = {
+        "torch_copy": (8, lambda: (gv.copy_(mv), 0)[1]),
+        "torch_add": (12, lambda: (torch.add(mv, vv, out=gv), 0)[1]),
+    }
+
+    def time_runs(table):
+        res_ = {}
+        for name, (bpe, fn) in table.items():
+            if fn() != 0:
+                raise RuntimeError(f"pattern {name} did not launch")
+            evs = []
+            for _ in range(5):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+            res_[name] = {"avg_ms": round(ms, 4), "bytes_per_elem": bpe,
+                          "gbps": round(bpe * n / (ms * 1e-3) / 1e9, 1)}
+        return res_
+    out = time_runs(runs)
+    vendor = time_runs(vendor_runs)
     rd, wr = out["read_only"]["gbps"], out["write_only"]["gbps"]
 
     def serial(r_bytes, w_bytes):
@@ -794,8 +807,10 @@ def pattern_ceilings(w, st, reps, kinds, per_kernel):
                    "grids, no arithmetic; median of 5 launches by HIP events.  read_only: the "
                    "reduce's P nontemporal streams; write_only: the fastest write shape "
                    "measured (plain 16-byte stores, 4 KB per workgroup); the serialised bound "
-                   "reads at read_only's and writes at write_only's rate",
+                   "reads at read_only's and writes at write_only's rate.  vendor_kernels: "
+                   "PyTorch's copy (g <- m) and add (g <- m + v) on the same buffers",
            "patterns": out,
+           "vendor_kernels": vendor,
            "serialised_bound_gbps": {"reduce": serial(2 * w.P, 4),
                                      "adamw": serial(16, 14 + (MX_BYTES if mx else 0))},
            "kernel_frac_of_pattern": {}}
