@@ -183,3 +183,19 @@ def test_adamw_step_counter_checks(lib):
     assert lib.zero_adamw_step(C.byref(a), None) == -2          # counter misaligned
     a.step_dev = fake + 8
     assert lib.zero_adamw_step_unfused(C.byref(a), fake, 1 << 30, None) == -1
+
+
+
+def test_header_compiles_as_c11():
+    """zero_step.h is plain C: the C program that drives the ABI in the GPU
+    tests (tests/c_abi/abi_roundtrip.c) compiles as pedantic C11 with every
+    warning an error (HIP's own headers as system headers)."""
+    import subprocess
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-pedantic", "-Werror", "-Wall", "-Wextra", "-fsyntax-only",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "oracle"), "-I", os.path.join(ROOT, "synth"),
+           "-isystem", os.path.join(rocm, "include"),
+           os.path.join(ROOT, "tests", "c_abi", "abi_roundtrip.c")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
