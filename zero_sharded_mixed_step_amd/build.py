@@ -30,15 +30,29 @@ PATTERNS_SOURCES = [os.path.join(HERE, "csrc", "zs_patterns.hip")]
 
 
 def _compile(sources, out, defines, verbose):
+    """Compiles `sources` into `out`, and writes the compiler's per-kernel
+    resource report (registers, scratch, occupancy) to out + RESOURCES."""
     tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines],
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, *sources]
+           "-Rpass-analysis=kernel-resource-usage", "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    remarks = [ln for ln in r.stderr.splitlines() if "kernel-resource-usage" in ln]
+    rest = "\n".join(ln for ln in r.stderr.splitlines() if "kernel-resource-usage" not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{rest}")
+    if verbose and rest.strip():
+        print(rest, flush=True)
+    with open(out + RESOURCES, "w") as fh:
+        fh.write("\n".join(remarks) + "\n")
     os.replace(tmp, out)
     return out
+
+
+# Suffix of the per-kernel resource report written beside each library.
+RESOURCES = ".resources.txt"
 
 
 def build(verbose: bool = False, out: str = LIB, defines=(), patterns: bool = True) -> str:
