@@ -208,7 +208,8 @@ def step_kernels(w):
     one-shot> (one-shot with P >= 4 above 2^27 elements a launch, where
     ShardStep passes the workspace, then a fold launch; else pipelined for
     P in {4, 8}), AdamW template <gradient source (-1: materialised g), P,
-    bf16 param, fused MXFP8, tiles per workgroup>."""
+    bf16 param, fused MXFP8, tiles per workgroup, first tiles loaded before
+    the gate>."""
     from zero_sharded_mixed_step_amd.step import ONESHOT_MIN
     path = _path_of(w)
     dt = 2 if w.mx_grads else (1 if w.grad_bf16 else 0)
@@ -220,9 +221,13 @@ def step_kernels(w):
     launches = -(-w.S // w.bucket) if w.bucket else 1
     mx = "true" if w.pack else "false"
     # AdamW tiles per workgroup: 2, or 1 where two would give fewer than two
-    # workgroups per compute unit (256 on MI355X)
-    u = 1 if -(-(-(-(-(-w.S // 8)) // 256)) // 2) < 2 * 256 else 2
-    mx = f"{mx}, {u}"
+    # workgroups per compute unit (256 on MI355X); the first tiles are loaded
+    # before the gate on grids of up to 128 workgroups per compute unit
+    ntiles = -(-(-(-w.S // 8)) // 256)
+    g2 = -(-ntiles // 2)
+    u = 1 if g2 < 2 * 256 else 2
+    early = "true" if u == 1 or g2 <= 128 * 256 else "false"
+    mx = f"{mx}, {u}, {early}"
     out = []
     fold = ("zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
             "adds the one-shot reduce's slots to the accumulator", launches)

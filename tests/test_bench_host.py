@@ -74,7 +74,7 @@ def test_counter_scaling(tmp_path, monkeypatch):
     1 GiB copy fixes f and w, averaged over dispatches per launch kind."""
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     copy = "__amd_rocclr_copyBuffer"
-    adamw = "void zs::adamw_kernel<-1, 1, true, true, 2>(zs::AdamParams)"
+    adamw = "void zs::adamw_kernel<-1, 1, true, true, 2, false>(zs::AdamParams)"
     red = "void zs::shard_reduce_kernel<1, 8, true, true, false>(zs::ReduceParams)"
     d = {k: str(tmp_path / k) for k in ("f", "w", "cf", "cw")}
     _write_counters(d["cf"], [(copy, 524288.0)])          # a copy reads half its bytes
@@ -128,14 +128,17 @@ def test_pass_structure_choice():
     ("30b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, false, true>"
                       "(zs::ReduceParams)",
                       "zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
-                      "void zs::adamw_kernel<-1, 1, true, true, 2>(zs::AdamParams)"]),
+                      "void zs::adamw_kernel<-1, 1, true, true, 2, false>(zs::AdamParams)"]),
     ("7b-shard-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, true, false>"
                      "(zs::ReduceParams)",
-                     "void zs::adamw_kernel<-1, 1, true, false, 2>(zs::AdamParams)"]),
+                     "void zs::adamw_kernel<-1, 1, true, false, 2, false>(zs::AdamParams)"]),
+    ("gpt2-small-p8", ["void zs::shard_reduce_kernel<1, 8, true, true, true, false>"
+                       "(zs::ReduceParams)",
+                       "void zs::adamw_kernel<-1, 1, true, false, 2, true>(zs::AdamParams)"]),
     ("1.3b-unsharded", ["void zs::shard_reduce_kernel<1, 1, false, true, false, false>"
                         "(zs::ReduceParams)",
-                        "void zs::adamw_kernel<1, 1, true, false, 2>(zs::AdamParams)"]),
-    ("flat-1m-p4", ["void zs::adamw_kernel<0, 4, true, false, 1>(zs::AdamParams)"]),
+                        "void zs::adamw_kernel<1, 1, true, false, 2, false>(zs::AdamParams)"]),
+    ("flat-1m-p4", ["void zs::adamw_kernel<0, 4, true, false, 1, true>(zs::AdamParams)"]),
 ])
 def test_step_kernel_names(name, kernels):
     """The kernels a step launches, named as rocprofv3 prints them, follow the
@@ -193,7 +196,7 @@ def test_placement_report_splits_the_two_placements(tmp_path, capsys):
     rows = []
     kinds = ["void zs::shard_reduce_kernel<1, 8, true, true, false, true>(zs::ReduceParams)",
              "zs::slot_fold_kernel(zero_norm_acc*, zero_norm_acc*)",
-             "void zs::adamw_kernel<-1, 1, true, true, 2>(zs::AdamParams)"] * 2
+             "void zs::adamw_kernel<-1, 1, true, true, 2, false>(zs::AdamParams)"] * 2
     for i, k in enumerate(kinds):
         rows.append({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": "X_sum",
                      "Counter_Value": 100 + i, "Start_Timestamp": 0,
