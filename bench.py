@@ -1185,6 +1185,10 @@ def measure(w, args, dev, legs=True, recycle=True):
         "bytes_per_param": sum(kinds.values()),
         "applied_steps": applied,
         "kernels": per_kernel,
+        **({"kernels_note": "a step this short is bound by the host's launches: the events "
+                            "around each pass also hold the GPU's wait for that pass's launch; "
+                            "the rocprofv3 kernel trace gives the kernels' own durations"}
+           if ms_per_step < 1.0 else {}),
         "standalone_kernels": standalone,
         "unfused_chain": unfused,
         "roofline": roof,
