@@ -34,7 +34,10 @@ struct Replicas {
 // 448 * 2^127 before rounding of an overflow to inf).  A NaN code (0x7F or
 // 0xFF) or the NaN scale byte 0xFF gives the quiet NaN 0x7FC00000 with the
 // code's sign, written out explicitly so the bits do not depend on how the
-// conversion or the multiply propagates a NaN.
+// conversion or the multiply propagates a NaN.  The eight codes are first
+// tested four at a time: a byte masked to 0x7F and plus one reaches 0x80
+// only when it was a NaN code, with no carry into the next byte; lanes with
+// neither a NaN code nor the NaN scale skip the per-element replacement.
 __device__ __forceinline__ void decode_mx8(uint32_t lo, uint32_t hi, uint32_t sb,
                                            float x[8]) {
   // (scale byte 0xFF: any finite factor; those results are replaced below)
@@ -49,11 +52,18 @@ __device__ __forceinline__ void decode_mx8(uint32_t lo, uint32_t hi, uint32_t sb
     x[4 * h + 1] = a[1] * f;
     x[4 * h + 2] = b[0] * f;
     x[4 * h + 3] = b[1] * f;
+  }
+  const uint32_t nan_bytes = (((lo & 0x7F7F7F7Fu) + 0x01010101u) |
+                              ((hi & 0x7F7F7F7Fu) + 0x01010101u)) & 0x80808080u;
+  if (sb == 0xFFu || nan_bytes != 0u) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t c = (w[h] >> (8 * q)) & 0xFFu;
-      if (sb == 0xFFu || (c & 0x7Fu) == 0x7Fu)
-        x[4 * h + q] = __uint_as_float(((c & 0x80u) << 24) | 0x7FC00000u);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t c = (w[h] >> (8 * q)) & 0xFFu;
+        if (sb == 0xFFu || (c & 0x7Fu) == 0x7Fu)
+          x[4 * h + q] = __uint_as_float(((c & 0x80u) << 24) | 0x7FC00000u);
+      }
     }
   }
 }
