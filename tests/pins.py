@@ -469,6 +469,38 @@ def _adamw_exact_element(g, coef, s, theta, m, v):
     return th, mi, vi
 
 
+def check_adamw_exact_brute_ieee_corners():
+    # 16-element vectors of finite IEEE corner values -- zeros of both signs,
+    # subnormal gradients and state, the edges of the normal range, large
+    # values short of overflow -- with beta1 = 0, full decay (lr * wd = 1)
+    # and clip coefficients down to a subnormal one: every binary32 result
+    # equals the exact simulation (which rounds subnormals exactly).
+    rng = np.random.default_rng(25)
+    n = 16
+    G = [0.0, -0.0, 1e-45, -1e-45, 1e-40, -3e-39, 1.1754942e-38, 1.17549435e-38, 1e-30,
+         -1e-20, 1e-3, -0.5, 1.0, 1e15, -3e15]
+    TH = [0.0, -0.0, 1e-45, -1e-40, 1.17549435e-38, 0.02, -1.5, 1e30]
+    M = [0.0, -0.0, 1e-45, -1e-40, 1e-30, 1e-3, -0.2, 1e20]
+    V = [0.0, 1e-45, 1e-40, 1.17549435e-38, 1e-20, 1e-6, 1.0, 1e30]
+    hypers = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (0.1, 0.0, 0.5, 1e-6, 0.0),
+              (1.0, 0.999, 0.0, 1e-6, 1.0)]
+    for lr, b1, b2, eps, wd in hypers:
+        master = rng.choice(np.array(TH, np.float32), n)
+        mm = rng.choice(np.array(M, np.float32), n)
+        vv = rng.choice(np.array(V, np.float32), n)
+        param = np.zeros(n, np.uint16)
+        for t, coef in ((1, 1.0), (2, 0.37), (5, float(np.float32(1e-40))), (6, 0.0)):
+            g = rng.choice(np.array(G, np.float32), n)
+            s = O.make_scalars(lr, b1, b2, eps, wd, t)
+            want = [_adamw_exact_element(g[i], np.float32(coef), s, master[i], mm[i], vv[i])
+                    for i in range(n)]
+            O.adamw(g, coef, s, master, mm, vv, param)
+            assert np.isfinite(master).all() and np.isfinite(mm).all() and np.isfinite(vv).all()
+            for i, (th, mi, vi) in enumerate(want):
+                assert (master[i], mm[i], vv[i]) == (np.float32(th), np.float32(mi),
+                                                     np.float32(vi)), (lr, t, i)
+
+
 def check_adamw_exact_brute():
     # 16-element vectors over several steps with nonzero moments and a clip
     # coefficient: every binary32 result equals the exact simulation, and the

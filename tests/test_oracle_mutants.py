@@ -60,6 +60,8 @@ MUTANTS = [
     ("m_mul_then_add", "float mi = fmaf(s->b1, m[i], t1);", "float mi = s->b1 * m[i] + t1;"),
     ("v_mul_then_add", "float vi = fmaf(s->b2, v[i], t3);", "float vi = s->b2 * v[i] + t3;"),
     ("update_mul_then_add", "th = fmaf(-s->step_size, u, th);", "th = -s->step_size * u + th;"),
+    ("gc_flushes_subnormals", "float gc = g[i] * coef;",
+     "float gc = g[i] * coef; if (fabsf(gc) < 1.17549435e-38f) gc = 0.0f;"),
     ("other_ranks_ignored", "for (int k = 0; k < n_extra; ++k) oracle_acc_add",
      "for (int k = 0; k < 0; ++k) oracle_acc_add"),
     ("bf16_ties_up", "up = (lo_mag & 1u) ? 1 : 0; /* tie", "up = 1; /* tie"),
