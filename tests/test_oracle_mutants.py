@@ -62,6 +62,8 @@ MUTANTS = [
     ("update_mul_then_add", "th = fmaf(-s->step_size, u, th);", "th = -s->step_size * u + th;"),
     ("gc_flushes_subnormals", "float gc = g[i] * coef;",
      "float gc = g[i] * coef; if (fabsf(gc) < 1.17549435e-38f) gc = 0.0f;"),
+    ("v_flushes_subnormals", "float vi = fmaf(s->b2, v[i], t3);",
+     "float vi = fmaf(s->b2, v[i], t3); if (vi < 1.17549435e-38f) vi = 0.0f;"),
     ("other_ranks_ignored", "for (int k = 0; k < n_extra; ++k) oracle_acc_add",
      "for (int k = 0; k < 0; ++k) oracle_acc_add"),
     ("bf16_ties_up", "up = (lo_mag & 1u) ? 1 : 0; /* tie", "up = 1; /* tie"),
