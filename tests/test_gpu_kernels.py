@@ -51,7 +51,7 @@ def test_device_generator_matches_host(zs, bf16):
 
 # ---------------------------------------------------------------- reduce --
 
-SIZES = [1, 7, 8, 17, 31, 33, 1024, 4097, 65536 + 13]
+SIZES = [1, 7, 8, 16, 17, 31, 32, 33, 1024, 4097, 65536 + 13]
 
 
 @pytest.mark.parametrize("P", [1, 2, 3, 4, 8, 16, 64])   # 64 = ZERO_MAX_REPLICAS
@@ -369,7 +369,7 @@ HP = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (0.1, 0.5, 0.75, 1e-3, 0.5)]
 @pytest.mark.parametrize("gated", [False, True])
 def test_adamw_multi_step(zs, source, gated):
     import torch
-    for n in (17, 4096 + 5, 70001):
+    for n in (16, 17, 31, 32, 33, 1024, 4096 + 5, 70001):
         for hp in HP:
             lr, b1, b2, eps, wd = hp
             if source == "grad_f32":
